@@ -1,0 +1,222 @@
+"""Benchmark of one tensor-parallel rank's hot path on one MI355X.
+
+One step = one pass of the whole path over one batch of synthetic inputs:
+  1. tp_mlp_fwd_bwd: one TP=8 rank's share of a Llama-3-70B-shaped GELU MLP,
+     forward + backward (T=8192, d=8192, f=3584, bf16 in, fp32 accumulate),
+     six MFMA GEMMs with the GELU / GELU' epilogues fused;
+  2. sharded_matmul_fwd_bwd: the same rank's inner-axis GEMM shard,
+     forward + backward (M=8192, K_r=1024, N=8192, bf16);
+  3. vocab_parallel_ce_fwd_bwd: 4096 positions x vocab 128256 split into 8
+     shards, bf16 logits, mean loss and dlogits.
+Inputs are resident in HBM before timing starts.  ``value`` is the MLP's
+fwd+bwd TFLOP/s (12*T*d*f algorithmic FLOP per call); the CE's algorithmic
+GB/s (2 bytes read + 2 bytes written per logit) and the inner GEMM's TFLOP/s
+are reported beside it.  Each call is timed with HIP events on the stream the
+library launches on.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+"""
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
+METRIC = "TP-rank MLP fwd+bwd TFLOP/s (% bf16 MFMA peak); vocab-CE HBM GB/s"
+
+MLP = dict(T=8192, d=8192, f=3584)
+INNER = dict(M=8192, K=1024, N=8192)
+CE = dict(T=4096, V=128256, parts=8)
+
+
+def kernel_source_digest():
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "megatron_mlp_fwd_amd", "csrc")
+    for name in sorted(os.listdir(csrc)):
+        with open(os.path.join(csrc, name), "rb") as f:
+            h.update(name.encode() + f.read())
+    return h.hexdigest()[:16]
+
+
+def stored_traffic(kernel):
+    """HBM bytes per launch measured with rocprofv3 counters for the current
+    kernel sources, or None when the sources changed since."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    try:
+        with open(path) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if t.get("kernel_source_digest") != kernel_source_digest():
+        return None
+    v = t.get(kernel)
+    return None if v is None else float(v)
+
+
+def cpu_baseline(budget_s=10.0):
+    """Time the fp64 oracle on a bounded sample of the MLP workload (a subset
+    of the tokens at the full 70B-rank d and f)."""
+    import numpy as np
+    import threadpoolctl
+    import torch
+
+    import oracle
+    import workloads
+
+    d, f = MLP["d"], MLP["f"]
+
+    def run(T):
+        x, w1, w2, gy = workloads.rank_mlp(T, d, f, seed=11, device="cpu")
+        xs = [t.float().numpy().astype(np.float64) for t in (x, w1, w2, gy)]
+        t0 = time.perf_counter()
+        oracle.mlp_fwd_bwd(*xs, "math")
+        return time.perf_counter() - t0
+
+    T = 64
+    dt = run(T)
+    T = int(min(MLP["T"], max(64, T * budget_s / max(dt, 1e-3))))
+    T -= T % 64
+    dt = run(T)
+    flops = 12.0 * T * d * f
+    threads = max([i.get("num_threads", 1) for i in threadpoolctl.threadpool_info()] + [1])
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+            "sample": f"oracle.mlp_fwd_bwd (NumPy fp64) on T={T} of the 8192 tokens at d={d}, f={f}, "
+                      f"{dt:.2f} s, {os.cpu_count()} host CPUs visible"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU: every simulated tensor-parallel rank runs on that device. "
+              "Runs on more than one GPU are not supported.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import megatron_mlp_fwd_amd as tpr
+    import workloads
+
+    tpr.load_library()
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+
+    x, w1, w2, gy = workloads.rank_mlp(MLP["T"], MLP["d"], MLP["f"], seed=0, device=dev)
+    a, b, g = workloads.inner_gemm(INNER["M"], INNER["K"], INNER["N"], seed=1, device=dev)
+    logits, labels = workloads.vocab_ce(T=CE["T"], V=CE["V"], seed=2, device=dev)
+    T, d, f = MLP["T"], MLP["d"], MLP["f"]
+    mlp_out = (torch.empty(T, d, device=dev), torch.empty(T, d, device=dev),
+               torch.empty(d, f, device=dev), torch.empty(f, d, device=dev))
+    mlp_ws = torch.empty(tpr.tp_mlp_workspace_bytes(1, torch.bfloat16, T, d, f), dtype=torch.uint8, device=dev)
+    M, K, N = INNER["M"], INNER["K"], INNER["N"]
+    inner_out = (torch.empty(M, N, device=dev), torch.empty(M, K, device=dev), torch.empty(K, N, device=dev))
+    ce_out = (torch.empty((), device=dev), torch.empty_like(logits), None)
+    ce_ws = torch.empty(tpr.vocab_parallel_ce_workspace_bytes(CE["parts"], CE["T"], CE["V"]), dtype=torch.uint8,
+                        device=dev)
+
+    def step(ev):
+        ev[0].record()
+        tpr.tp_mlp_fwd_bwd(1, x, w1, w2, gy, "math", out=mlp_out, workspace=mlp_ws)
+        ev[1].record()
+        tpr.sharded_matmul_fwd_bwd("inner", 1, a, b, g, out=inner_out)
+        ev[2].record()
+        tpr.vocab_parallel_ce_fwd_bwd(CE["parts"], logits, labels, out=ce_out, workspace=ce_ws)
+        ev[3].record()
+
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(max(args.steps, args.warmup))]
+    for i in range(args.warmup):
+        step(events[i])
+    torch.cuda.synchronize()
+    t_start = torch.cuda.Event(enable_timing=True)
+    t_end = torch.cuda.Event(enable_timing=True)
+    t_start.record()
+    for i in range(args.steps):
+        step(events[i])
+    t_end.record()
+    torch.cuda.synchronize()
+
+    total_ms = t_start.elapsed_time(t_end)
+    mlp_ms = [e[0].elapsed_time(e[1]) for e in events[:args.steps]]
+    inner_ms = [e[1].elapsed_time(e[2]) for e in events[:args.steps]]
+    ce_ms = [e[2].elapsed_time(e[3]) for e in events[:args.steps]]
+    avg = lambda v: sum(v) / len(v)
+
+    mlp_flop = 12.0 * T * d * f
+    inner_flop = 6.0 * M * K * N
+    ce_bytes = 4.0 * CE["T"] * CE["V"]
+    mlp_tflops = mlp_flop / (avg(mlp_ms) * 1e-3) / 1e12
+    inner_tflops = inner_flop / (avg(inner_ms) * 1e-3) / 1e12
+    ce_gbs = ce_bytes / (avg(ce_ms) * 1e-3) / 1e9
+
+    # Dominant kernel: the bf16 MFMA GEMM (6 launches per MLP call, each
+    # 2*T*d*f FLOP; the tp=1 call launches nothing else).
+    gemm_launch_ms = avg(mlp_ms) / 6.0
+    gemm_achieved = (2.0 * T * d * f) / (gemm_launch_ms * 1e-3) / 1e12
+    gemm_traffic = stored_traffic("gemm_bf16_mlp_bytes_per_launch")
+    ce_traffic = stored_traffic("vocab_ce_bytes_per_launch")
+
+    line = {
+        "metric": METRIC,
+        "value": round(mlp_tflops, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(total_ms / args.steps, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": "llama3_70b_tp8_rank_mlp_fwd_bwd + llama3_70b_tp8_inner_gemm_fwd_bwd + "
+                        "vocab_ce_t4096_v128256_p8",
+            "mlp": dict(MLP, tp_simulated=1, w_layout="math"),
+            "inner_gemm": INNER,
+            "vocab_ce": CE,
+            "parallelism": "tp8 rank share on 1 GPU",
+        },
+        "mlp_pct_of_bf16_peak": round(100.0 * mlp_tflops / PEAK_BF16_TFLOPS, 2),
+        "mlp_ms": round(avg(mlp_ms), 4),
+        "inner_gemm_tflops": round(inner_tflops, 2),
+        "inner_gemm_ms": round(avg(inner_ms), 4),
+        "vocab_ce_gbs": round(ce_gbs, 1),
+        "vocab_ce_pct_of_hbm_peak": round(100.0 * ce_gbs / PEAK_HBM_GBS, 2),
+        "vocab_ce_ms": round(avg(ce_ms), 4),
+        "roofline": {
+            "kernel": "gemm_bf16_kernel (MLP GEMMs, average of the 6 launches)",
+            "bound": "mfma",
+            "achieved": round(gemm_achieved, 2),
+            "peak": PEAK_BF16_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": round(gemm_achieved / PEAK_BF16_TFLOPS, 4),
+            "traffic": gemm_traffic,
+        },
+        "roofline_ce": {
+            "kernel": "ce_fast_kernel + loss_mean_kernel (one call)",
+            "bound": "hbm",
+            "achieved": round(ce_gbs, 1),
+            "peak": PEAK_HBM_GBS,
+            "unit": "GB/s",
+            "frac": round(ce_gbs / PEAK_HBM_GBS, 4),
+            "traffic": ce_traffic,
+        },
+        "kernel_source_digest": kernel_source_digest(),
+    }
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline()
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,180 @@
+/*
+ * tprank.h -- C ABI of libtprank: one tensor-parallel rank's hot path on an
+ * AMD Instinct MI355X (gfx950), with every simulated rank computed on the one
+ * GPU.
+ *
+ * Sources of the operations (page titles as printed, then the section):
+ *   [GEMM]  "Sharded GEMM与Backprop：行、列、内维三种切分"
+ *           sections 题意与假设 (assumptions) and 解题路线 (solution route)
+ *   [CARDS] "多卡张量：拆开计算，再合回同一结果"
+ *           sections 01 / COLUMN THEN ROW, 02 / BACKWARD, 04 / VOCABULARY SHARDS
+ *   [TP]    "第 6 课：张量并行 TP"
+ *           section 1 (column- and row-parallel linears) and 2.A (the MLP)
+ *
+ * Conventions shared by every entry point
+ *   - Tensors are dense and row-major (C order); sizes are element counts.
+ *   - Every data pointer is a DEVICE pointer owned by the caller; the library
+ *     never allocates, frees or keeps a pointer after a call returns.
+ *   - `ws` is a caller-owned device workspace of at least the size that the
+ *     matching *_workspace_bytes() returns (NULL is allowed when that size is
+ *     0).  Its contents on entry do not matter and are clobbered.
+ *   - `stream` is a hipStream_t (NULL = the default stream).  All work is
+ *     enqueued on it; calls return without waiting for the GPU.
+ *   - dtype: TPR_F32 (inputs are float) or TPR_BF16 (inputs are bfloat16
+ *     bit patterns stored as uint16).  Products accumulate in fp32.
+ *   - Return value: TPR_OK or one of the TPR_ERR_* codes.  Every argument is
+ *     validated on the host before anything is enqueued, so a non-zero
+ *     status leaves every output untouched.  tprank_last_error() then holds
+ *     a message (per thread).  TPR_ERR_HIP reports a failed launch.
+ *   - Device pointers to bf16 data must be 2-byte aligned and to fp32 data
+ *     4-byte aligned; 16-byte alignment (with row lengths that are multiples
+ *     of 8) selects the vectorised kernels, anything else the element-wise
+ *     ones.  Results do not depend on which is chosen beyond fp32 rounding
+ *     order.
+ */
+#ifndef TPRANK_H
+#define TPRANK_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* ---- status codes ------------------------------------------------------ */
+#define TPR_OK 0
+#define TPR_ERR_SHAPE 1      /* shape mismatch / negative size ([GEMM] reference code: ValueError('shape')) */
+#define TPR_ERR_PARTITION 2  /* parts < 1, bad axis or rank ([GEMM] reference code: ValueError('partition')) */
+#define TPR_ERR_DTYPE 3      /* unknown dtype or weight layout */
+#define TPR_ERR_WORKSPACE 4  /* ws_bytes smaller than the *_workspace_bytes() value */
+#define TPR_ERR_NULLPTR 5    /* a pointer that must be non-NULL is NULL */
+#define TPR_ERR_HIP 6        /* a HIP launch failed */
+
+/* ---- enumerations ------------------------------------------------------ */
+#define TPR_ROWS 0     /* split M: A and G by rows        ([GEMM] 解题路线 step 2) */
+#define TPR_COLUMNS 1  /* split N: B and G by columns     ([GEMM] 解题路线 step 3) */
+#define TPR_INNER 2    /* split K: A by columns, B by rows ([GEMM] 解题路线 step 4) */
+
+#define TPR_F32 0
+#define TPR_BF16 1
+
+#define TPR_W_MATH 0   /* w1 is d x f and w2 is f x d: y = gelu(x w1) w2      ([TP] 2.A) */
+#define TPR_W_TORCH 1  /* w1 is (f, d) and w2 is (d, f): y = gelu(x w1^T) w2^T ([TP] 1, solution code) */
+
+/* ---- shard planning ----------------------------------------------------- */
+/*
+ * Half-open index range [*begin, *end) of shard `rank` when `n` indices are
+ * split into `parts` contiguous shards.  [GEMM] 题意与假设 allows uneven and
+ * empty shards; 手动走一遍 fixes the order (K=5 over 2 parts is 3 then 2):
+ * every shard gets floor(n/parts) indices and the first n mod parts shards
+ * one more.  Host-only, touches no device.
+ * Errors: TPR_ERR_SHAPE if n < 0; TPR_ERR_PARTITION if parts < 1 or rank is
+ * outside [0, parts); TPR_ERR_NULLPTR if begin or end is NULL.
+ */
+int tprank_shard_range(int64_t n, int parts, int rank, int64_t* begin, int64_t* end);
+
+/* ---- sharded matrix multiply, forward and backward ------------------- */
+/*
+ * Bytes of workspace sharded_matmul_fwd_bwd() needs: one fp32 partial per
+ * rank for the output that the chosen axis sums (dB for rows, dA for
+ * columns, Y for inner), or 0 when parts == 1.  Returns 0 for invalid
+ * arguments (the call itself then reports the error).
+ */
+size_t sharded_matmul_workspace_bytes(int axis, int parts, int dtype, int64_t M, int64_t K, int64_t N);
+
+/*
+ * [GEMM] 题意与假设 / 解题路线: with A (M x K), B (K x N) and the upstream
+ * gradient G (M x N) of the loss L = <G, A B>, simulate `parts` ranks split
+ * along `axis` and produce the full logical results
+ *     Y = A B (M x N),  dA = G B^T (M x K),  dB = A^T G (K x N),
+ * all fp32.  Each rank computes its local products with the bf16 (MFMA) or
+ * fp32 GEMM kernels; outputs the axis stacks are written in place by each
+ * rank (no concatenation kernel), outputs the axis sums are reduced from
+ * per-rank fp32 partials in a fixed rank order (the simulated all-reduce).
+ * Empty shards are skipped; an inner rank with no K indices contributes the
+ * zero product.  Zero-size M, K or N are valid (outputs of zero size are not
+ * touched; dA/dB/Y of non-zero size whose contraction is empty are zeroed).
+ *   A, B, G: inputs in `dtype`; Y, dA, dB: fp32 outputs (may be NULL only if
+ *   they have zero elements).
+ * Errors: SHAPE (negative size), PARTITION (parts < 1 or unknown axis),
+ * DTYPE, NULLPTR, WORKSPACE, HIP.
+ */
+int sharded_matmul_fwd_bwd(int axis, int parts, int dtype, int64_t M, int64_t K, int64_t N,
+                           const void* A, const void* B, const void* G,
+                           float* Y, float* dA, float* dB,
+                           void* ws, size_t ws_bytes, void* stream);
+
+/* ---- column-then-row tensor-parallel GELU MLP ------------------------- */
+/*
+ * Bytes of workspace tp_mlp_fwd_bwd() needs: the pre-activation and the
+ * activation (T x f each, in `dtype`; the pre-activation buffer is reused
+ * for the gradient at the pre-activation), plus, when tp > 1, the tp
+ * full-shape fp32 partials of y and of dx.  Returns 0 for invalid arguments.
+ */
+size_t tp_mlp_workspace_bytes(int tp, int dtype, int64_t T, int64_t d, int64_t f);
+
+/*
+ * [TP] 2.A and [CARDS] 01 / 02: `tp` ranks each own hidden columns [lo, hi)
+ * of W1 (column-parallel) and the same rows of W2 (row-parallel).  Per rank,
+ *   forward:  P_r = x W1_r;  H_r = gelu(P_r) (exact erf, fused in the GEMM
+ *             epilogue);  Z_r = H_r W2_r, a full-shape T x d partial;
+ *   backward (L = sum(y * gy), the same gy used once by every rank):
+ *             dW2_r = H_r^T gy;  dZ_r = (gy W2_r^T) * gelu'(P_r) (fused);
+ *             dW1_r = x^T dZ_r;  dx_r = dZ_r W1_r^T;
+ * then y = sum_r Z_r and dx = sum_r dx_r (the MLP's one reduction each way,
+ * fixed rank order).  With tp == 1 the call computes one rank's share: pass
+ * the rank's weight shards (w1 d x f_r, w2 f_r x d in TPR_W_MATH) and y, dx
+ * are that rank's partials Z_r, dx_r.  For TPR_BF16 the activation and the
+ * pre-activation gradient are rounded to bf16 (they are GEMM operands); the
+ * pre-activation is kept in bf16.
+ *   x, gy: T x d in `dtype` (leading dims of an activation flatten into T);
+ *   w1, w2: weights in `dtype` and `w_layout`;
+ *   y, dx: fp32 T x d;  dw1, dw2: fp32, same shapes/layout as w1, w2.
+ * Errors: SHAPE, PARTITION (tp < 1), DTYPE (dtype or w_layout), NULLPTR,
+ * WORKSPACE, HIP.
+ */
+int tp_mlp_fwd_bwd(int tp, int dtype, int w_layout, int64_t T, int64_t d, int64_t f,
+                   const void* x, const void* w1, const void* w2, const void* gy,
+                   float* y, float* dx, float* dw1, float* dw2,
+                   void* ws, size_t ws_bytes, void* stream);
+
+/* ---- vocabulary-parallel cross-entropy -------------------------------- */
+/*
+ * Bytes of workspace vocab_parallel_ce_fwd_bwd() needs (the T per-row
+ * losses, fp32).  Returns 0 for invalid arguments.
+ */
+size_t vocab_parallel_ce_workspace_bytes(int parts, int64_t T, int64_t V);
+
+/*
+ * [CARDS] 04 / VOCABULARY SHARDS, for T positions with logits z (T x V) and
+ * targets y, the vocabulary split into `parts` contiguous shards V_r:
+ *   m_r = max_{V_r} z,  m = max_r m_r,
+ *   s_r = sum_{V_r} exp(z - m),  s = sum_r s_r,
+ *   t_r = [y in V_r] (z_y - m),  L_i = log s - sum_r t_r,
+ *   loss = (1/T) sum_i L_i  (mean over positions, no smoothing),
+ *   dlogits_ij = (exp(z_ij - m_i)/s_i - [j = y_i]) / T.
+ * One fused kernel keeps each row on chip: it reads the logits once and
+ * writes dlogits once; the per-shard statistics are combined in a fixed
+ * order.
+ *   logits: T x V in `dtype`;  labels: T int64 with 0 <= y < V (not checked
+ *   on the device; a label outside that range gives an unspecified loss and
+ *   no target term, but no out-of-bounds access);
+ *   loss: one fp32 on the device;  dlogits: T x V in `dtype`;
+ *   shard_stats: NULL, or T x parts x 3 fp32 receiving (m_r, s_r, t_r)
+ *   (m_r = -inf and s_r = 0 for an empty shard).
+ * T == 0 writes loss = 0.  V must be >= 1 when T > 0.
+ * Errors: SHAPE, PARTITION, DTYPE, NULLPTR, WORKSPACE, HIP.
+ */
+int vocab_parallel_ce_fwd_bwd(int parts, int dtype, int64_t T, int64_t V,
+                              const void* logits, const int64_t* labels,
+                              float* loss, void* dlogits, float* shard_stats,
+                              void* ws, size_t ws_bytes, void* stream);
+
+/* Message for the last non-zero status returned on the calling thread. */
+const char* tprank_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* TPRANK_H */

@@ -1,0 +1,216 @@
+"""ctypes binding of libtprank (include/tprank.h), same entry-point names.
+
+Argument marshalling only: checks that tensors live on the GPU, are
+contiguous and have the shapes and dtypes the C ABI expects (the library
+cannot see buffer sizes), allocates outputs and the workspace with torch's
+caching allocator, and passes raw device pointers plus the current HIP stream.
+Every step of the computation runs in the library's HIP kernels; there is no
+fallback of any kind -- if the library is missing, loading fails.
+"""
+import ctypes
+import os
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libtprank.so")
+
+TPR_OK, TPR_ERR_SHAPE, TPR_ERR_PARTITION, TPR_ERR_DTYPE, TPR_ERR_WORKSPACE, TPR_ERR_NULLPTR, TPR_ERR_HIP = range(7)
+AXES = {"rows": 0, "columns": 1, "inner": 2}
+DTYPES = {torch.float32: 0, torch.bfloat16: 1}
+W_LAYOUTS = {"math": 0, "torch": 1}
+
+_lib = None
+
+_i64, _i32, _vp, _sz = ctypes.c_int64, ctypes.c_int, ctypes.c_void_p, ctypes.c_size_t
+_SIGS = {
+    "tprank_shard_range": (_i32, [_i64, _i32, _i32, ctypes.POINTER(_i64), ctypes.POINTER(_i64)]),
+    "sharded_matmul_workspace_bytes": (_sz, [_i32, _i32, _i32, _i64, _i64, _i64]),
+    "sharded_matmul_fwd_bwd": (_i32, [_i32, _i32, _i32, _i64, _i64, _i64, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
+    "tp_mlp_workspace_bytes": (_sz, [_i32, _i32, _i64, _i64, _i64]),
+    "tp_mlp_fwd_bwd": (_i32, [_i32, _i32, _i32, _i64, _i64, _i64, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
+    "vocab_parallel_ce_workspace_bytes": (_sz, [_i32, _i64, _i64]),
+    "vocab_parallel_ce_fwd_bwd": (_i32, [_i32, _i32, _i64, _i64, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
+    "tprank_last_error": (ctypes.c_char_p, []),
+}
+
+
+class TprError(RuntimeError):
+    """A non-zero status from libtprank; ``code`` is the TPR_ERR_* value."""
+
+    def __init__(self, code, msg):
+        super().__init__(f"libtprank error {code}: {msg}")
+        self.code = code
+
+
+def load_library(path=LIB_PATH):
+    """Load libtprank.so once (torch is imported first so that both share
+    the HIP runtime already in the process)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(path):
+            raise RuntimeError(f"{path} is not built; run `python -m megatron_mlp_fwd_amd.build`")
+        lib = ctypes.CDLL(path)
+        for name, (res, args) in _SIGS.items():
+            fn = getattr(lib, name)
+            fn.restype, fn.argtypes = res, args
+        _lib = lib
+    return _lib
+
+
+def _check(status):
+    if status != TPR_OK:
+        raise TprError(status, load_library().tprank_last_error().decode())
+
+
+def _ptr(t):
+    return None if t is None or t.numel() == 0 else t.data_ptr()
+
+
+def _stream(stream):
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return s.cuda_stream
+
+
+def _need(t, name, shape, dtype, device):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be on a GPU")
+    if device is not None and t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    if t.dtype != dtype:
+        raise ValueError(f"{name} has dtype {t.dtype}, expected {dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def _workspace(nbytes, device, workspace):
+    if nbytes == 0:
+        return None, 0
+    if workspace is not None:
+        if workspace.device != device or not workspace.is_contiguous() or workspace.numel() * workspace.element_size() < nbytes:
+            raise ValueError(f"workspace must be a contiguous tensor of >= {nbytes} bytes on {device}")
+        return workspace, workspace.numel() * workspace.element_size()
+    return torch.empty(nbytes, dtype=torch.uint8, device=device), nbytes
+
+
+def shard_range(n, parts, rank):
+    """[begin, end) of shard ``rank`` of ``n`` indices over ``parts`` shards."""
+    b, e = _i64(), _i64()
+    _check(load_library().tprank_shard_range(n, parts, rank, ctypes.byref(b), ctypes.byref(e)))
+    return b.value, e.value
+
+
+def sharded_matmul_workspace_bytes(axis, parts, dtype, M, K, N):
+    return load_library().sharded_matmul_workspace_bytes(AXES.get(axis, axis), parts, DTYPES[dtype], M, K, N)
+
+
+def sharded_matmul_fwd_bwd(axis, parts, A, B, G, out=None, workspace=None, stream=None):
+    """Y = A B, dA = G B^T, dB = A^T G computed by ``parts`` simulated ranks
+    split along ``axis`` ('rows', 'columns' or 'inner').  Returns fp32
+    (Y, dA, dB); ``out`` may supply the three output tensors."""
+    lib = load_library()
+    ax = AXES[axis] if isinstance(axis, str) else int(axis)
+    if A.dim() != 2 or B.dim() != 2:
+        raise ValueError("A and B must be 2-D")
+    M, K = A.shape
+    N = B.shape[1]
+    dt = A.dtype
+    if dt not in DTYPES:
+        raise ValueError(f"unsupported dtype {dt}")
+    dev = A.device
+    _need(A, "A", (M, K), dt, dev)
+    _need(B, "B", (K, N), dt, dev)
+    _need(G, "G", (M, N), dt, dev)
+    if out is None:
+        out = (torch.empty(M, N, device=dev), torch.empty(M, K, device=dev), torch.empty(K, N, device=dev))
+    Y, dA, dB = out
+    _need(Y, "Y", (M, N), torch.float32, dev)
+    _need(dA, "dA", (M, K), torch.float32, dev)
+    _need(dB, "dB", (K, N), torch.float32, dev)
+    ws, wsb = _workspace(lib.sharded_matmul_workspace_bytes(ax, parts, DTYPES[dt], M, K, N), dev, workspace)
+    with torch.cuda.device(dev):
+        _check(lib.sharded_matmul_fwd_bwd(ax, parts, DTYPES[dt], M, K, N, _ptr(A), _ptr(B), _ptr(G), _ptr(Y),
+                                          _ptr(dA), _ptr(dB), _ptr(ws), wsb, _stream(stream)))
+    return Y, dA, dB
+
+
+def tp_mlp_workspace_bytes(tp, dtype, T, d, f):
+    return load_library().tp_mlp_workspace_bytes(tp, DTYPES[dtype], T, d, f)
+
+
+def tp_mlp_fwd_bwd(tp, x, w1, w2, gy, w_layout="math", out=None, workspace=None, stream=None):
+    """Column-then-row GELU MLP over ``tp`` simulated ranks, forward and
+    backward for L = sum(y * gy).  ``x``/``gy`` are (..., d) with leading dims
+    flattened into tokens.  Returns fp32 (y, dx, dw1, dw2) with y, dx shaped
+    like x and dw1, dw2 like w1, w2."""
+    lib = load_library()
+    layout = W_LAYOUTS[w_layout]
+    dt = x.dtype
+    if dt not in DTYPES:
+        raise ValueError(f"unsupported dtype {dt}")
+    if w1.dim() != 2 or w2.dim() != 2:
+        raise ValueError("w1 and w2 must be 2-D")
+    d, f = (w1.shape[0], w1.shape[1]) if layout == 0 else (w1.shape[1], w1.shape[0])
+    wshape1, wshape2 = ((d, f), (f, d)) if layout == 0 else ((f, d), (d, f))
+    if x.dim() < 1 or x.shape[-1] != d:
+        raise ValueError(f"x must be (..., {d})")
+    T = 1
+    for n in x.shape[:-1]:
+        T *= n
+    dev = x.device
+    xs = tuple(x.shape)
+    _need(x, "x", xs, dt, dev)
+    _need(gy, "gy", xs, dt, dev)
+    _need(w1, "w1", wshape1, dt, dev)
+    _need(w2, "w2", wshape2, dt, dev)
+    if out is None:
+        out = (torch.empty(xs, device=dev), torch.empty(xs, device=dev),
+               torch.empty(wshape1, device=dev), torch.empty(wshape2, device=dev))
+    y, dx, dw1, dw2 = out
+    _need(y, "y", xs, torch.float32, dev)
+    _need(dx, "dx", xs, torch.float32, dev)
+    _need(dw1, "dw1", wshape1, torch.float32, dev)
+    _need(dw2, "dw2", wshape2, torch.float32, dev)
+    ws, wsb = _workspace(lib.tp_mlp_workspace_bytes(tp, DTYPES[dt], T, d, f), dev, workspace)
+    with torch.cuda.device(dev):
+        _check(lib.tp_mlp_fwd_bwd(tp, DTYPES[dt], layout, T, d, f, _ptr(x), _ptr(w1), _ptr(w2), _ptr(gy), _ptr(y),
+                                  _ptr(dx), _ptr(dw1), _ptr(dw2), _ptr(ws), wsb, _stream(stream)))
+    return y, dx, dw1, dw2
+
+
+def vocab_parallel_ce_workspace_bytes(parts, T, V):
+    return load_library().vocab_parallel_ce_workspace_bytes(parts, T, V)
+
+
+def vocab_parallel_ce_fwd_bwd(parts, logits, labels, shard_stats=False, out=None, workspace=None, stream=None):
+    """Mean cross-entropy over the rows of ``logits`` (T x V) with the
+    vocabulary split into ``parts`` shards, and its gradient.  Returns
+    (loss: 0-d fp32 tensor, dlogits: like logits, stats: T x parts x 3 fp32
+    of (m_r, s_r, t_r) or None)."""
+    lib = load_library()
+    dt = logits.dtype
+    if dt not in DTYPES:
+        raise ValueError(f"unsupported dtype {dt}")
+    if logits.dim() != 2:
+        raise ValueError("logits must be 2-D")
+    T, V = logits.shape
+    dev = logits.device
+    _need(logits, "logits", (T, V), dt, dev)
+    _need(labels, "labels", (T,), torch.int64, dev)
+    if out is None:
+        out = (torch.empty((), device=dev), torch.empty(T, V, dtype=dt, device=dev),
+               torch.empty(T, parts, 3, device=dev) if shard_stats else None)
+    loss, dlogits, stats = out
+    _need(loss, "loss", (), torch.float32, dev)
+    _need(dlogits, "dlogits", (T, V), dt, dev)
+    if stats is not None:
+        _need(stats, "shard_stats", (T, parts, 3), torch.float32, dev)
+    ws, wsb = _workspace(lib.vocab_parallel_ce_workspace_bytes(parts, T, V), dev, workspace)
+    with torch.cuda.device(dev):
+        _check(lib.vocab_parallel_ce_fwd_bwd(parts, DTYPES[dt], T, V, _ptr(logits), _ptr(labels), loss.data_ptr(),
+                                             _ptr(dlogits), _ptr(stats), _ptr(ws), wsb, _stream(stream)))
+    return loss, dlogits, stats

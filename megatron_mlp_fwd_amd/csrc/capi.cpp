@@ -1,0 +1,308 @@
+// C ABI of libtprank (declared in include/tprank.h): argument validation,
+// shard planning, workspace carving and the launch sequence of each entry
+// point.  All validation happens before the first launch, so an error leaves
+// every output untouched.  Nothing here allocates device memory.
+#include <climits>
+#include <cstdarg>
+#include <cstdio>
+#include <string>
+#include <vector>
+
+#include "common.h"
+#include "tprank.h"
+
+namespace {
+
+thread_local std::string g_err;
+
+int fail(int code, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  return code;
+}
+
+int hip_fail(hipError_t e, const char* what) {
+  return fail(TPR_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+int64_t esize(int dtype) { return dtype == TPR_BF16 ? 2 : 4; }
+bool dtype_ok(int dtype) { return dtype == TPR_F32 || dtype == TPR_BF16; }
+bool dim_ok(int64_t n) { return n >= 0 && n <= INT_MAX; }
+
+// Shard rule of the sharded GEMM page (题意与假设 / 手动走一遍): floor(n/P)
+// indices each, one more for the first n mod P shards.
+void shard_of(int64_t n, int parts, int r, int64_t* lo, int64_t* hi) {
+  const int64_t base = n / parts, extra = n % parts;
+  *lo = r * base + (r < extra ? r : extra);
+  *hi = *lo + base + (r < extra ? 1 : 0);
+}
+
+const char* cb(const void* p) { return static_cast<const char*>(p); }
+
+tpr::GemmProb prob(const void* A, int64_t sa_m, int64_t sa_k, const void* B, int64_t sb_k, int64_t sb_n, void* C,
+                   int64_t ldc, int64_t M, int64_t N, int64_t K, const void* aux_in = nullptr,
+                   void* aux_out = nullptr) {
+  tpr::GemmProb p{};
+  p.A = A;
+  p.B = B;
+  p.C = C;
+  p.aux_in = aux_in;
+  p.aux_out = aux_out;
+  p.sa_m = sa_m;
+  p.sa_k = sa_k;
+  p.sb_k = sb_k;
+  p.sb_n = sb_n;
+  p.ldc = ldc;
+  p.M = (int)M;
+  p.N = (int)N;
+  p.K = (int)K;
+  return p;
+}
+
+// Run a list of same-layout problems as grouped launches of up to
+// kMaxGroup problems; problems with no output are dropped.
+hipError_t run_gemms(const std::vector<tpr::GemmProb>& ps, int dtype, bool a_kmajor, bool b_kmajor, int epi,
+                     hipStream_t s) {
+  std::vector<tpr::GemmProb> live;
+  for (const auto& p : ps)
+    if (p.M > 0 && p.N > 0) live.push_back(p);
+  for (size_t i = 0; i < live.size(); i += tpr::kMaxGroup) {
+    tpr::GemmBatch b{};
+    b.count = (int)std::min<size_t>(tpr::kMaxGroup, live.size() - i);
+    for (int j = 0; j < b.count; ++j) b.p[j] = live[i + j];
+    const hipError_t e = dtype == TPR_BF16 ? tpr::launch_gemm_bf16(b, a_kmajor, b_kmajor, epi, s)
+                                           : tpr::launch_gemm_f32(b, a_kmajor, b_kmajor, epi, s);
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
+}
+
+// Finish an output that the split sums: reduce the partials in slot order,
+// or zero it when no rank contributed (empty contraction).
+hipError_t finish_sum(float* out, int64_t rows, int64_t cols, const float* slots, int nslots, int64_t stride,
+                      bool direct, hipStream_t s) {
+  if (rows <= 0 || cols <= 0) return hipSuccess;
+  if (nslots == 0) return tpr::launch_fill_zero(out, rows, cols, cols, s);
+  if (direct) return hipSuccess;
+  return tpr::launch_reduce_partials(slots, nslots, stride, out, rows * cols, s);
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* tprank_last_error(void) { return g_err.c_str(); }
+
+int tprank_shard_range(int64_t n, int parts, int rank, int64_t* begin, int64_t* end) {
+  if (begin == nullptr || end == nullptr) return fail(TPR_ERR_NULLPTR, "begin/end must not be NULL");
+  if (n < 0) return fail(TPR_ERR_SHAPE, "n must be >= 0 (got %lld)", (long long)n);
+  if (parts < 1) return fail(TPR_ERR_PARTITION, "parts must be >= 1 (got %d)", parts);
+  if (rank < 0 || rank >= parts) return fail(TPR_ERR_PARTITION, "rank %d outside [0, %d)", rank, parts);
+  shard_of(n, parts, rank, begin, end);
+  return TPR_OK;
+}
+
+// ---------------------------------------------------------------- sharded GEMM
+size_t sharded_matmul_workspace_bytes(int axis, int parts, int dtype, int64_t M, int64_t K, int64_t N) {
+  if (parts < 1 || axis < TPR_ROWS || axis > TPR_INNER || !dtype_ok(dtype) || M < 0 || K < 0 || N < 0) return 0;
+  if (parts == 1) return 0;
+  const int64_t sz = axis == TPR_ROWS ? K * N : axis == TPR_COLUMNS ? M * K : M * N;
+  return (size_t)parts * align256((size_t)sz * 4);
+}
+
+int sharded_matmul_fwd_bwd(int axis, int parts, int dtype, int64_t M, int64_t K, int64_t N, const void* A,
+                           const void* B, const void* G, float* Y, float* dA, float* dB, void* ws, size_t ws_bytes,
+                           void* stream) {
+  if (!dim_ok(M) || !dim_ok(K) || !dim_ok(N))
+    return fail(TPR_ERR_SHAPE, "M, K, N must be in [0, 2^31) (got %lld, %lld, %lld)", (long long)M, (long long)K,
+                (long long)N);
+  if (parts < 1) return fail(TPR_ERR_PARTITION, "parts must be >= 1 (got %d)", parts);
+  if (axis < TPR_ROWS || axis > TPR_INNER) return fail(TPR_ERR_PARTITION, "unknown axis %d", axis);
+  if (!dtype_ok(dtype)) return fail(TPR_ERR_DTYPE, "unknown dtype %d", dtype);
+  if ((M * K > 0 && (A == nullptr || dA == nullptr)) || (K * N > 0 && (B == nullptr || dB == nullptr)) ||
+      (M * N > 0 && (G == nullptr || Y == nullptr)))
+    return fail(TPR_ERR_NULLPTR, "a non-empty input or output pointer is NULL");
+  const size_t need = sharded_matmul_workspace_bytes(axis, parts, dtype, M, K, N);
+  if (ws_bytes < need || (need > 0 && ws == nullptr))
+    return fail(TPR_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", need, ws_bytes);
+
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const int64_t e = esize(dtype);
+  const int64_t sum_n = axis == TPR_ROWS ? K * N : axis == TPR_COLUMNS ? M * K : M * N;
+  const int64_t stride = (int64_t)(align256((size_t)sum_n * 4) / 4);
+  float* slots = static_cast<float*>(ws);
+  const bool direct = parts == 1;
+  int nslots = 0;
+  std::vector<tpr::GemmProb> fy, fda, fdb;
+
+  for (int r = 0; r < parts; ++r) {
+    int64_t lo, hi;
+    if (axis == TPR_ROWS) {
+      shard_of(M, parts, r, &lo, &hi);
+      const int64_t m = hi - lo;
+      if (m == 0) continue;
+      // Y_r = A_r B and dA_r = G_r B^T land in their row slices; dB_r = A_r^T G_r is a partial.
+      fy.push_back(prob(cb(A) + lo * K * e, K, 1, B, N, 1, Y + lo * N, N, m, N, K));
+      fda.push_back(prob(cb(G) + lo * N * e, N, 1, B, 1, N, dA + lo * K, K, m, K, N));
+      float* dst = direct ? dB : slots + nslots * stride;
+      fdb.push_back(prob(cb(A) + lo * K * e, 1, K, cb(G) + lo * N * e, N, 1, dst, N, K, N, m));
+      ++nslots;
+    } else if (axis == TPR_COLUMNS) {
+      shard_of(N, parts, r, &lo, &hi);
+      const int64_t n = hi - lo;
+      if (n == 0) continue;
+      // Y_r = A B_r and dB_r = A^T G_r land in their column slices; dA_r = G_r B_r^T is a partial.
+      fy.push_back(prob(A, K, 1, cb(B) + lo * e, N, 1, Y + lo, N, M, n, K));
+      fdb.push_back(prob(A, 1, K, cb(G) + lo * e, N, 1, dB + lo, N, K, n, M));
+      float* dst = direct ? dA : slots + nslots * stride;
+      fda.push_back(prob(cb(G) + lo * e, N, 1, cb(B) + lo * e, 1, N, dst, K, M, K, n));
+      ++nslots;
+    } else {
+      shard_of(K, parts, r, &lo, &hi);
+      const int64_t k = hi - lo;
+      if (k == 0) continue;
+      // Y_r = A_r B_r is a partial; dA_r = G B_r^T and dB_r = A_r^T G land in their K slices.
+      float* dst = direct ? Y : slots + nslots * stride;
+      fy.push_back(prob(cb(A) + lo * e, K, 1, cb(B) + lo * N * e, N, 1, dst, N, M, N, k));
+      fda.push_back(prob(G, N, 1, cb(B) + lo * N * e, 1, N, dA + lo, K, M, k, N));
+      fdb.push_back(prob(cb(A) + lo * e, 1, K, G, N, 1, dB + lo * N, N, k, N, M));
+      ++nslots;
+    }
+  }
+
+  hipError_t he;
+  if ((he = run_gemms(fy, dtype, true, false, tpr::EPI_F32, s)) != hipSuccess) return hip_fail(he, "Y GEMM");
+  if ((he = run_gemms(fda, dtype, true, true, tpr::EPI_F32, s)) != hipSuccess) return hip_fail(he, "dA GEMM");
+  if ((he = run_gemms(fdb, dtype, false, false, tpr::EPI_F32, s)) != hipSuccess) return hip_fail(he, "dB GEMM");
+  if (axis == TPR_ROWS)
+    he = finish_sum(dB, K, N, slots, nslots, stride, direct, s);
+  else if (axis == TPR_COLUMNS)
+    he = finish_sum(dA, M, K, slots, nslots, stride, direct, s);
+  else
+    he = finish_sum(Y, M, N, slots, nslots, stride, direct, s);
+  if (he != hipSuccess) return hip_fail(he, "partial-sum reduction");
+  return TPR_OK;
+}
+
+// ---------------------------------------------------------------- TP MLP
+size_t tp_mlp_workspace_bytes(int tp, int dtype, int64_t T, int64_t d, int64_t f) {
+  if (tp < 1 || !dtype_ok(dtype) || T < 0 || d < 0 || f < 0) return 0;
+  size_t b = 2 * align256((size_t)(T * f * esize(dtype)));
+  if (tp > 1) b += 2 * (size_t)tp * align256((size_t)(T * d * 4));
+  return b;
+}
+
+int tp_mlp_fwd_bwd(int tp, int dtype, int w_layout, int64_t T, int64_t d, int64_t f, const void* x, const void* w1,
+                   const void* w2, const void* gy, float* y, float* dx, float* dw1, float* dw2, void* ws,
+                   size_t ws_bytes, void* stream) {
+  if (!dim_ok(T) || !dim_ok(d) || !dim_ok(f))
+    return fail(TPR_ERR_SHAPE, "T, d, f must be in [0, 2^31) (got %lld, %lld, %lld)", (long long)T, (long long)d,
+                (long long)f);
+  if (tp < 1) return fail(TPR_ERR_PARTITION, "tp must be >= 1 (got %d)", tp);
+  if (!dtype_ok(dtype)) return fail(TPR_ERR_DTYPE, "unknown dtype %d", dtype);
+  if (w_layout != TPR_W_MATH && w_layout != TPR_W_TORCH) return fail(TPR_ERR_DTYPE, "unknown w_layout %d", w_layout);
+  if ((T * d > 0 && (x == nullptr || gy == nullptr || y == nullptr || dx == nullptr)) ||
+      (d * f > 0 && (w1 == nullptr || w2 == nullptr || dw1 == nullptr || dw2 == nullptr)))
+    return fail(TPR_ERR_NULLPTR, "a non-empty input or output pointer is NULL");
+  const size_t need = tp_mlp_workspace_bytes(tp, dtype, T, d, f);
+  if (ws_bytes < need || (need > 0 && ws == nullptr))
+    return fail(TPR_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", need, ws_bytes);
+
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const int64_t e = esize(dtype);
+  char* wsb = static_cast<char*>(ws);
+  char* pre = wsb;                                            // T x f pre-activation, then dZ in place
+  char* act = wsb + align256((size_t)(T * f * e));            // T x f activation
+  const int64_t pstride = (int64_t)(align256((size_t)(T * d * 4)) / 4);
+  float* zpart = reinterpret_cast<float*>(wsb + 2 * align256((size_t)(T * f * e)));
+  float* xpart = zpart + (int64_t)tp * pstride;
+  const bool direct = tp == 1;
+  const bool math = w_layout == TPR_W_MATH;
+  int nslots = 0;
+  std::vector<tpr::GemmProb> f1, f2, gw2, gh, gw1, gx;
+
+  for (int r = 0; r < tp; ++r) {
+    int64_t lo, hi;
+    shard_of(f, tp, r, &lo, &hi);
+    const int64_t fr = hi - lo;
+    if (fr == 0) continue;
+    char* Pr = pre + T * lo * e;  // rank-local T x fr blocks
+    char* Hr = act + T * lo * e;
+    float* ydst = direct ? y : zpart + nslots * pstride;
+    float* xdst = direct ? dx : xpart + nslots * pstride;
+    if (math) {  // w1 d x f, w2 f x d
+      f1.push_back(prob(x, d, 1, cb(w1) + lo * e, f, 1, Pr, fr, T, fr, d, nullptr, Hr));
+      f2.push_back(prob(Hr, fr, 1, cb(w2) + lo * d * e, d, 1, ydst, d, T, d, fr));
+      gw2.push_back(prob(Hr, 1, fr, gy, d, 1, dw2 + lo * d, d, fr, d, T));
+      gh.push_back(prob(gy, d, 1, cb(w2) + lo * d * e, 1, d, Pr, fr, T, fr, d, Pr));
+      gw1.push_back(prob(x, 1, d, Pr, fr, 1, dw1 + lo, f, d, fr, T));
+      gx.push_back(prob(Pr, fr, 1, cb(w1) + lo * e, 1, f, xdst, d, T, d, fr));
+    } else {  // w1 (f, d), w2 (d, f)
+      f1.push_back(prob(x, d, 1, cb(w1) + lo * d * e, 1, d, Pr, fr, T, fr, d, nullptr, Hr));
+      f2.push_back(prob(Hr, fr, 1, cb(w2) + lo * e, 1, f, ydst, d, T, d, fr));
+      gw2.push_back(prob(gy, 1, d, Hr, fr, 1, dw2 + lo, f, d, fr, T));
+      gh.push_back(prob(gy, d, 1, cb(w2) + lo * e, f, 1, Pr, fr, T, fr, d, Pr));
+      gw1.push_back(prob(Pr, 1, fr, x, d, 1, dw1 + lo * d, d, fr, d, T));
+      gx.push_back(prob(Pr, fr, 1, cb(w1) + lo * d * e, d, 1, xdst, d, T, d, fr));
+    }
+    ++nslots;
+  }
+
+  hipError_t he;
+  // Forward: column-parallel GEMM with the GELU epilogue, then the row-parallel GEMM.
+  if ((he = run_gemms(f1, dtype, true, !math, tpr::EPI_GELU, s)) != hipSuccess) return hip_fail(he, "fc1 GEMM");
+  if ((he = run_gemms(f2, dtype, true, !math, tpr::EPI_F32, s)) != hipSuccess) return hip_fail(he, "fc2 GEMM");
+  // Backward: weight gradient of fc2, activation gradient with the GELU' epilogue,
+  // weight gradient of fc1, input gradient.
+  if ((he = run_gemms(gw2, dtype, false, false, tpr::EPI_F32, s)) != hipSuccess) return hip_fail(he, "dW2 GEMM");
+  if ((he = run_gemms(gh, dtype, true, math, tpr::EPI_DGELU, s)) != hipSuccess) return hip_fail(he, "dH GEMM");
+  if ((he = run_gemms(gw1, dtype, false, false, tpr::EPI_F32, s)) != hipSuccess) return hip_fail(he, "dW1 GEMM");
+  if ((he = run_gemms(gx, dtype, true, math, tpr::EPI_F32, s)) != hipSuccess) return hip_fail(he, "dx GEMM");
+  // The block's one reduction each way: y = sum_r Z_r, dx = sum_r dx_r.
+  if ((he = finish_sum(y, T, d, zpart, nslots, pstride, direct, s)) != hipSuccess) return hip_fail(he, "y reduction");
+  if ((he = finish_sum(dx, T, d, xpart, nslots, pstride, direct, s)) != hipSuccess)
+    return hip_fail(he, "dx reduction");
+  return TPR_OK;
+}
+
+// ---------------------------------------------------------------- vocab CE
+size_t vocab_parallel_ce_workspace_bytes(int parts, int64_t T, int64_t V) {
+  if (parts < 1 || T < 0 || V < 0) return 0;
+  return align256((size_t)T * 4);
+}
+
+int vocab_parallel_ce_fwd_bwd(int parts, int dtype, int64_t T, int64_t V, const void* logits, const int64_t* labels,
+                              float* loss, void* dlogits, float* shard_stats, void* ws, size_t ws_bytes,
+                              void* stream) {
+  if (T < 0 || V < 0 || T > UINT_MAX || V / 8 > INT_MAX)
+    return fail(TPR_ERR_SHAPE, "T and V out of range (got %lld, %lld)", (long long)T, (long long)V);
+  if (T > 0 && V == 0) return fail(TPR_ERR_SHAPE, "V must be >= 1 when T > 0");
+  if (parts < 1) return fail(TPR_ERR_PARTITION, "parts must be >= 1 (got %d)", parts);
+  if (!dtype_ok(dtype)) return fail(TPR_ERR_DTYPE, "unknown dtype %d", dtype);
+  if (loss == nullptr || (T > 0 && (logits == nullptr || labels == nullptr || dlogits == nullptr)))
+    return fail(TPR_ERR_NULLPTR, "loss, logits, labels or dlogits is NULL");
+  const size_t need = vocab_parallel_ce_workspace_bytes(parts, T, V);
+  if (ws_bytes < need || (need > 0 && ws == nullptr))
+    return fail(TPR_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", need, ws_bytes);
+  tpr::CeArgs a{};
+  a.logits = logits;
+  a.labels = labels;
+  a.dlogits = dlogits;
+  a.shard_stats = shard_stats;
+  a.row_loss = static_cast<float*>(ws);
+  a.loss = loss;
+  a.T = T;
+  a.V = V;
+  a.parts = parts;
+  a.dtype = dtype;
+  const hipError_t he = tpr::launch_vocab_ce(a, static_cast<hipStream_t>(stream));
+  if (he != hipSuccess) return hip_fail(he, "vocab CE launch");
+  return TPR_OK;
+}
+
+}  // extern "C"

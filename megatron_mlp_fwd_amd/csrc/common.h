@@ -1,0 +1,68 @@
+// Internal declarations shared by the libtprank sources (not part of the ABI).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+#include <stddef.h>
+
+namespace tpr {
+
+// ---------------------------------------------------------------- GEMM
+// One GEMM problem C(m, n) = sum_k A(m, k) B(k, n) with
+//   A(m, k) = A[m * sa_m + k * sa_k],  B(k, n) = B[k * sb_k + n * sb_n],
+//   C(m, n) = C[m * ldc + n]   (aux_in / aux_out use the same ldc).
+// Either sa_k == 1 (A "k-major") or sa_m == 1 (A "m-major"); likewise B is
+// k-major (sb_k == 1) or n-major (sb_n == 1).  The launcher picks the kernel
+// instance from the layout flags, never from the strides alone.
+struct GemmProb {
+  const void* A;
+  const void* B;
+  void* C;
+  const void* aux_in;   // epilogue input (pre-activation for EPI_DGELU)
+  void* aux_out;        // epilogue second output (activation for EPI_GELU)
+  int64_t sa_m, sa_k, sb_k, sb_n, ldc;
+  int M, N, K;
+  int tiles_m, tiles_n;  // filled by the launcher
+  int tile_start;        // first flattened block index of this problem
+};
+
+constexpr int kMaxGroup = 8;  // problems per grouped launch
+
+struct GemmBatch {
+  GemmProb p[kMaxGroup];
+  int count;
+  int total_tiles;
+};
+
+enum Epilogue {
+  EPI_F32 = 0,    // C (fp32) = acc
+  EPI_GELU = 1,   // C (compute dtype) = acc  [pre-activation], aux_out = gelu(acc)
+  EPI_DGELU = 2,  // C (compute dtype) = acc * gelu'(aux_in)    [in place allowed]
+};
+
+// A group of problems sharing dtype, layout and epilogue.  Launchers return
+// hipSuccess or the launch error.
+hipError_t launch_gemm_bf16(GemmBatch& b, bool a_kmajor, bool b_kmajor, int epi, hipStream_t s);
+hipError_t launch_gemm_f32(GemmBatch& b, bool a_kmajor, bool b_kmajor, int epi, hipStream_t s);
+
+// ---------------------------------------------------------------- reductions
+// out[i] = sum_{s < nslots} part[s * stride + i], summed in slot order.
+hipError_t launch_reduce_partials(const float* part, int nslots, int64_t stride, float* out, int64_t n,
+                                  hipStream_t s);
+hipError_t launch_fill_zero(float* out, int64_t rows, int64_t cols, int64_t ld, hipStream_t s);
+
+// ---------------------------------------------------------------- vocab CE
+struct CeArgs {
+  const void* logits;
+  const int64_t* labels;
+  void* dlogits;
+  float* shard_stats;  // nullable, T x parts x 3
+  float* row_loss;     // workspace, T floats
+  float* loss;         // device scalar
+  int64_t T, V;
+  int parts;
+  int dtype;  // TPR_F32 / TPR_BF16
+};
+hipError_t launch_vocab_ce(const CeArgs& a, hipStream_t s);
+
+}  // namespace tpr

@@ -1,0 +1,353 @@
+// Vocabulary-parallel cross-entropy, forward and backward, for T positions
+// with the vocabulary split into `parts` contiguous shards.
+//
+// Multi-card tensor page ("多卡张量：拆开计算，再合回同一结果"), section
+// 04 / VOCABULARY SHARDS: each shard r finds its local maximum m_r; the
+// global maximum m combines them; each shard sums exp(z - m) over its range
+// (s_r) and, if it owns the target, contributes z_y - m (t_r); the loss is
+// log(sum s_r) - sum t_r and the gradient is exp(z - m)/s minus the one-hot
+// target.  The workload averages over positions, so every row's gradient
+// carries 1/T.
+//
+// Fast path (bf16, shard edges on 8-element boundaries, up to 16 shards):
+// one 1024-thread workgroup per row holds the whole row in registers (16
+// slots of 16 bytes per thread; a slot is a 1024-vector run inside one
+// shard), so the logits are read from HBM once and dlogits written once --
+// the kernel is bound by HBM bandwidth (4 bytes per logit).  Per-shard
+// statistics are reduced per wave (shuffles) and across waves in LDS in a
+// fixed order; the cross-shard combine ("all-reduce" of max, then of the
+// sums) is a loop over the shard slots in rank order.
+//
+// General path (fp32 logits, any shard layout or count): one 256-thread
+// workgroup per row, three passes over the row (max per shard, sum and
+// target per shard, gradient).  Same arithmetic, the logits are re-read.
+//
+// A final single-workgroup kernel averages the per-row losses in a fixed
+// order (fp64 accumulation).
+#include "common.h"
+
+namespace tpr {
+namespace {
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int CE_NT = 1024;
+constexpr int CE_NW = CE_NT / 64;
+constexpr int CE_SLOTS = 16;
+constexpr int CE_PMAX = 16;
+constexpr float LOG2E = 1.4426950408889634f;
+
+struct CeSlots {
+  int nslot;
+  int P;
+  int shard[CE_SLOTS];  // shard of each slot, non-decreasing
+  int vbeg[CE_SLOTS];   // first 8-logit vector of the slot within the row
+  int nv[CE_SLOTS];     // vectors in the slot (<= CE_NT)
+  int64_t sbeg[CE_PMAX + 1];
+};
+
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
+  return v;
+}
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+  return v;
+}
+
+__device__ __forceinline__ float lo16(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float hi16(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+__device__ __forceinline__ uint32_t pack_bf16(float a, float b) {
+  const uint32_t x = __builtin_bit_cast(uint16_t, (__bf16)a);
+  const uint32_t y = __builtin_bit_cast(uint16_t, (__bf16)b);
+  return x | (y << 16);
+}
+__device__ __forceinline__ float elem(const u32x4& v, int e) {
+  const uint32_t w = v[e >> 1];
+  return (e & 1) ? hi16(w) : lo16(w);
+}
+
+__global__ __launch_bounds__(CE_NT, 1) void ce_fast_kernel(const uint16_t* __restrict__ logits,
+                                                          const int64_t* __restrict__ labels,
+                                                          uint16_t* __restrict__ dlogits, float* __restrict__ row_loss,
+                                                          float* __restrict__ stats, int64_t V, float invT,
+                                                          const CeSlots S) {
+  __shared__ float red_max[CE_NW][CE_PMAX];
+  __shared__ float red_sum[CE_NW][CE_PMAX];
+  __shared__ float sh_m[CE_PMAX], sh_s[CE_PMAX];
+  __shared__ float sh_t;
+
+  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+  const int64_t row = blockIdx.x;
+  const uint16_t* __restrict__ z = logits + row * V;
+  uint16_t* __restrict__ dz = dlogits + row * V;
+  const int64_t y = labels[row];
+
+  if (tid < CE_NW * CE_PMAX) {
+    (&red_max[0][0])[tid] = -INFINITY;
+    (&red_sum[0][0])[tid] = 0.f;
+  }
+  if (tid == 0) sh_t = 0.f;
+
+  // Load the row once: slot s, lane tid owns vector vbeg[s] + tid.  Idle
+  // lanes hold bf16 -inf, which drops out of the max and contributes exp = 0.
+  u32x4 v[CE_SLOTS];
+#pragma unroll
+  for (int s = 0; s < CE_SLOTS; ++s) {
+    const bool on = s < S.nslot && tid < S.nv[s];
+    v[s] = on ? *reinterpret_cast<const u32x4*>(z + 8 * ((int64_t)S.vbeg[s] + tid))
+              : u32x4{0xff80ff80u, 0xff80ff80u, 0xff80ff80u, 0xff80ff80u};
+  }
+  __syncthreads();
+
+  // Per-shard maxima m_r: running max over the slots of one shard, flushed
+  // (wave reduce, one LDS word per wave) when the slot's shard changes.
+  {
+    float run = -INFINITY;
+    int cur = S.shard[0];
+#pragma unroll
+    for (int s = 0; s < CE_SLOTS; ++s) {
+      if (s >= S.nslot) continue;
+      if (S.shard[s] != cur) {
+        const float w = wave_max(run);
+        if (lane == 0) red_max[wid][cur] = w;
+        run = -INFINITY;
+        cur = S.shard[s];
+      }
+      float lm = fmaxf(fmaxf(lo16(v[s][0]), hi16(v[s][0])), fmaxf(lo16(v[s][1]), hi16(v[s][1])));
+      lm = fmaxf(lm, fmaxf(fmaxf(lo16(v[s][2]), hi16(v[s][2])), fmaxf(lo16(v[s][3]), hi16(v[s][3]))));
+      run = fmaxf(run, lm);
+    }
+    if (S.nslot > 0) {
+      const float w = wave_max(run);
+      if (lane == 0) red_max[wid][cur] = w;
+    }
+  }
+  __syncthreads();
+  if (tid < S.P) {
+    float mr = -INFINITY;
+    for (int w = 0; w < CE_NW; ++w) mr = fmaxf(mr, red_max[w][tid]);
+    sh_m[tid] = mr;
+  }
+  __syncthreads();
+  float m = -INFINITY;
+  for (int r = 0; r < S.P; ++r) m = fmaxf(m, sh_m[r]);  // all-reduce(max)
+  const float mL = m * LOG2E;
+
+  // Per-shard sums s_r with the global maximum, and the target term.
+  const int64_t vy = y >> 3;
+  const int ey = (int)(y & 7);
+  {
+    float run = 0.f;
+    int cur = S.shard[0];
+#pragma unroll
+    for (int s = 0; s < CE_SLOTS; ++s) {
+      if (s >= S.nslot) continue;
+      if (S.shard[s] != cur) {
+        const float w = wave_sum(run);
+        if (lane == 0) red_sum[wid][cur] = w;
+        run = 0.f;
+        cur = S.shard[s];
+      }
+      float ls = 0.f;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) ls += __builtin_amdgcn_exp2f(elem(v[s], e) * LOG2E - mL);
+      run += ls;
+      if ((int64_t)S.vbeg[s] + tid == vy && tid < S.nv[s]) sh_t = elem(v[s], ey) - m;
+    }
+    if (S.nslot > 0) {
+      const float w = wave_sum(run);
+      if (lane == 0) red_sum[wid][cur] = w;
+    }
+  }
+  __syncthreads();
+  if (tid < S.P) {
+    float sr = 0.f;
+    for (int w = 0; w < CE_NW; ++w) sr += red_sum[w][tid];
+    sh_s[tid] = sr;
+  }
+  __syncthreads();
+  float ssum = 0.f;
+  for (int r = 0; r < S.P; ++r) ssum += sh_s[r];  // all-reduce(sum), rank order
+  const float t = sh_t;
+  if (tid == 0) row_loss[row] = logf(ssum) - t;
+  if (stats != nullptr && tid < S.P) {
+    const bool owns = y >= S.sbeg[tid] && y < S.sbeg[tid + 1];
+    float* st = stats + (row * S.P + tid) * 3;
+    st[0] = sh_m[tid];
+    st[1] = sh_s[tid];
+    st[2] = owns ? t : 0.f;
+  }
+
+  // Gradient: (exp(z - m) / s - [j == y]) / T, rounded to bf16, written once.
+  const float scale = invT / ssum;
+#pragma unroll
+  for (int s = 0; s < CE_SLOTS; ++s) {
+    if (s < S.nslot && tid < S.nv[s]) {
+      const int64_t vi = (int64_t)S.vbeg[s] + tid;
+      float g[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) g[e] = __builtin_amdgcn_exp2f(elem(v[s], e) * LOG2E - mL) * scale;
+      if (vi == vy) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+          if (e == ey) g[e] -= invT;
+      }
+      *reinterpret_cast<u32x4*>(dz + 8 * vi) =
+          u32x4{pack_bf16(g[0], g[1]), pack_bf16(g[2], g[3]), pack_bf16(g[4], g[5]), pack_bf16(g[6], g[7])};
+    }
+  }
+}
+
+// ---------------------------------------------------------------- general path
+template <typename T>
+__device__ __forceinline__ float ld_logit(const T* p, int64_t j);
+template <>
+__device__ __forceinline__ float ld_logit<float>(const float* p, int64_t j) { return p[j]; }
+template <>
+__device__ __forceinline__ float ld_logit<uint16_t>(const uint16_t* p, int64_t j) {
+  return __uint_as_float((uint32_t)p[j] << 16);
+}
+template <typename T>
+__device__ __forceinline__ void st_grad(T* p, int64_t j, float g);
+template <>
+__device__ __forceinline__ void st_grad<float>(float* p, int64_t j, float g) { p[j] = g; }
+template <>
+__device__ __forceinline__ void st_grad<uint16_t>(uint16_t* p, int64_t j, float g) {
+  p[j] = __builtin_bit_cast(uint16_t, (__bf16)g);
+}
+
+// Block-wide reduction of 256 threads; every thread gets the result.
+template <bool MAX>
+__device__ __forceinline__ float block_reduce(float v, float* scratch) {
+  v = MAX ? wave_max(v) : wave_sum(v);
+  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+  __syncthreads();  // scratch reuse across calls
+  if (lane == 0) scratch[wid] = v;
+  __syncthreads();
+  float r = scratch[0];
+  for (int w = 1; w < 4; ++w) r = MAX ? fmaxf(r, scratch[w]) : r + scratch[w];
+  return r;
+}
+
+template <typename T>
+__global__ __launch_bounds__(256) void ce_general_kernel(const T* __restrict__ logits,
+                                                         const int64_t* __restrict__ labels, T* __restrict__ dlogits,
+                                                         float* __restrict__ row_loss, float* __restrict__ stats,
+                                                         int64_t V, int P, float invT) {
+  __shared__ float scratch[4];
+  const int tid = threadIdx.x;
+  const int64_t row = blockIdx.x;
+  const T* __restrict__ z = logits + row * V;
+  T* __restrict__ dz = dlogits + row * V;
+  const int64_t y = labels[row];
+  const int64_t base = V / P, extra = V % P;
+
+  float m = -INFINITY;
+  for (int r = 0; r < P; ++r) {
+    const int64_t lo = r * base + (r < extra ? r : extra), hi = lo + base + (r < extra ? 1 : 0);
+    float loc = -INFINITY;
+    for (int64_t j = lo + tid; j < hi; j += 256) loc = fmaxf(loc, ld_logit(z, j));
+    const float mr = block_reduce<true>(loc, scratch);
+    m = fmaxf(m, mr);
+    if (stats != nullptr && tid == 0) stats[(row * P + r) * 3 + 0] = mr;
+  }
+  const float mL = m * LOG2E;
+  float ssum = 0.f, tsum = 0.f;
+  for (int r = 0; r < P; ++r) {
+    const int64_t lo = r * base + (r < extra ? r : extra), hi = lo + base + (r < extra ? 1 : 0);
+    float loc = 0.f;
+    for (int64_t j = lo + tid; j < hi; j += 256) loc += __builtin_amdgcn_exp2f(ld_logit(z, j) * LOG2E - mL);
+    const float sr = block_reduce<false>(loc, scratch);
+    const float tr = (y >= lo && y < hi) ? ld_logit(z, y) - m : 0.f;
+    ssum += sr;
+    tsum += tr;
+    if (stats != nullptr && tid == 0) {
+      stats[(row * P + r) * 3 + 1] = sr;
+      stats[(row * P + r) * 3 + 2] = tr;
+    }
+  }
+  if (tid == 0) row_loss[row] = logf(ssum) - tsum;
+  const float scale = invT / ssum;
+  for (int64_t j = tid; j < V; j += 256) {
+    float g = __builtin_amdgcn_exp2f(ld_logit(z, j) * LOG2E - mL) * scale;
+    if (j == y) g -= invT;
+    st_grad(dz, j, g);
+  }
+}
+
+__global__ __launch_bounds__(1024) void loss_mean_kernel(const float* __restrict__ row_loss, int64_t T,
+                                                         float* __restrict__ loss) {
+  __shared__ double part[16];
+  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+  double acc = 0.0;
+  for (int64_t i = tid; i < T; i += 1024) acc += (double)row_loss[i];
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) acc += __shfl_xor(acc, o, 64);
+  if (lane == 0) part[wid] = acc;
+  __syncthreads();
+  if (tid == 0) {
+    double s = 0.0;
+    for (int w = 0; w < 16; ++w) s += part[w];
+    loss[0] = T > 0 ? (float)(s / (double)T) : 0.f;
+  }
+}
+
+bool aligned16(const void* p) { return reinterpret_cast<uintptr_t>(p) % 16 == 0; }
+
+}  // namespace
+
+hipError_t launch_vocab_ce(const CeArgs& a, hipStream_t s) {
+  if (a.T > 0) {
+    const float invT = (float)(1.0 / (double)a.T);
+    const int64_t base = a.V / a.parts, extra = a.V % a.parts;
+    // Fast path eligibility and slot table.
+    bool fast = a.dtype == 1 && a.V % 8 == 0 && a.parts <= CE_PMAX && aligned16(a.logits) && aligned16(a.dlogits);
+    CeSlots S{};
+    S.P = a.parts;
+    if (fast) {
+      for (int r = 0; r <= a.parts && fast; ++r) {
+        const int64_t lo = r * base + (r < extra ? r : extra);
+        S.sbeg[r] = r < a.parts ? lo : a.V;
+        if (S.sbeg[r] % 8 != 0) fast = false;
+      }
+      for (int r = 0; r < a.parts && fast; ++r) {
+        int64_t vb = S.sbeg[r] / 8, nv = (S.sbeg[r + 1] - S.sbeg[r]) / 8;
+        while (nv > 0) {
+          if (S.nslot == CE_SLOTS) {
+            fast = false;
+            break;
+          }
+          const int64_t take = nv < CE_NT ? nv : CE_NT;
+          S.shard[S.nslot] = r;
+          S.vbeg[S.nslot] = (int)vb;
+          S.nv[S.nslot] = (int)take;
+          ++S.nslot;
+          vb += take;
+          nv -= take;
+        }
+      }
+    }
+    if (fast) {
+      hipLaunchKernelGGL(ce_fast_kernel, dim3((unsigned)a.T), dim3(CE_NT), 0, s,
+                         static_cast<const uint16_t*>(a.logits), a.labels, static_cast<uint16_t*>(a.dlogits),
+                         a.row_loss, a.shard_stats, a.V, invT, S);
+    } else if (a.dtype == 1) {
+      hipLaunchKernelGGL(ce_general_kernel<uint16_t>, dim3((unsigned)a.T), dim3(256), 0, s,
+                         static_cast<const uint16_t*>(a.logits), a.labels, static_cast<uint16_t*>(a.dlogits),
+                         a.row_loss, a.shard_stats, a.V, a.parts, invT);
+    } else {
+      hipLaunchKernelGGL(ce_general_kernel<float>, dim3((unsigned)a.T), dim3(256), 0, s,
+                         static_cast<const float*>(a.logits), a.labels, static_cast<float*>(a.dlogits), a.row_loss,
+                         a.shard_stats, a.V, a.parts, invT);
+    }
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  hipLaunchKernelGGL(loss_mean_kernel, dim3(1), dim3(1024), 0, s, a.row_loss, a.T, a.loss);
+  return hipGetLastError();
+}
+
+}  // namespace tpr

@@ -75,7 +75,7 @@ def _tokens(x, d):
     x = np.asarray(x, dtype=np.float64)
     if x.ndim < 1 or x.shape[-1] != d:
         raise ValueError("shape")
-    return x.reshape(-1, d)
+    return x.reshape(int(np.prod(x.shape[:-1])), d)
 
 
 def _from_math(dW1, dW2, w_layout):

@@ -1,0 +1,104 @@
+"""The C ABI library on the CPU: it loads, exports what the header declares,
+its host-side shard planner matches the oracle bit for bit, and it rejects
+invalid arguments before touching the GPU (CPU only, no compute calls)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import oracle
+from megatron_mlp_fwd_amd import binding
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "tprank.h")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(binding.LIB_PATH):
+        pytest.skip("libtprank.so is not built")
+    return binding.load_library()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\*?\s+\*?(\w+)\s*\(", text, flags=re.M)))
+
+
+def test_header_declares_the_entry_points():
+    names = declared_functions()
+    for n in ("sharded_matmul_fwd_bwd", "tp_mlp_fwd_bwd", "vocab_parallel_ce_fwd_bwd", "tprank_shard_range",
+              "tprank_last_error"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol(lib):
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+        ctypes.cast(getattr(lib, name), ctypes.c_void_p)
+
+
+def test_shard_range_matches_oracle_bit_for_bit(lib):
+    for n in list(range(0, 40)) + [128256, 14336, 28672, 8192, 1792, 3584, 2**31 - 1]:
+        for parts in list(range(1, 20)) + [64, 1000]:
+            want = oracle.shard_ranges(n, parts)
+            got = [binding.shard_range(n, parts, r) for r in range(parts)]
+            assert got == want, (n, parts)
+
+
+def test_walkthrough_split(lib):
+    assert [binding.shard_range(5, 2, r) for r in range(2)] == [(0, 3), (3, 5)]
+
+
+@pytest.mark.parametrize("args,code", [
+    ((-1, 2, 0), binding.TPR_ERR_SHAPE),
+    ((5, 0, 0), binding.TPR_ERR_PARTITION),
+    ((5, 2, 2), binding.TPR_ERR_PARTITION),
+    ((5, 2, -1), binding.TPR_ERR_PARTITION),
+])
+def test_shard_range_errors(lib, args, code):
+    b, e = ctypes.c_int64(), ctypes.c_int64()
+    assert lib.tprank_shard_range(*args, ctypes.byref(b), ctypes.byref(e)) == code
+    assert lib.tprank_last_error()
+
+
+def test_workspace_sizes(lib):
+    assert lib.sharded_matmul_workspace_bytes(0, 1, 0, 3, 5, 4) == 0
+    assert lib.sharded_matmul_workspace_bytes(0, 2, 0, 3, 5, 4) == 2 * 256     # rows: dB partials 5 x 4 fp32
+    assert lib.sharded_matmul_workspace_bytes(2, 8, 1, 8192, 8192, 8192) == 8 * 8192 * 8192 * 4
+    assert lib.sharded_matmul_workspace_bytes(3, 2, 0, 3, 5, 4) == 0            # invalid axis
+    assert lib.tp_mlp_workspace_bytes(1, 1, 8192, 8192, 3584) == 2 * 8192 * 3584 * 2
+    assert lib.tp_mlp_workspace_bytes(4, 0, 16, 64, 256) == 2 * 16 * 256 * 4 + 2 * 4 * 16 * 64 * 4
+    assert lib.vocab_parallel_ce_workspace_bytes(8, 4096, 128256) == 4096 * 4
+
+
+N = None
+
+
+def test_sharded_matmul_rejects_bad_arguments(lib):
+    f = lib.sharded_matmul_fwd_bwd
+    assert f(0, 1, 0, -1, 5, 4, N, N, N, N, N, N, N, 0, N) == binding.TPR_ERR_SHAPE
+    assert f(0, 0, 0, 3, 5, 4, N, N, N, N, N, N, N, 0, N) == binding.TPR_ERR_PARTITION
+    assert f(3, 2, 0, 3, 5, 4, N, N, N, N, N, N, N, 0, N) == binding.TPR_ERR_PARTITION
+    assert f(0, 2, 7, 3, 5, 4, N, N, N, N, N, N, N, 0, N) == binding.TPR_ERR_DTYPE
+    assert f(0, 2, 0, 3, 5, 4, N, N, N, N, N, N, N, 0, N) == binding.TPR_ERR_NULLPTR
+    p = ctypes.c_void_p(16)  # never dereferenced: validation stops first
+    assert f(0, 2, 0, 3, 5, 4, p, p, p, p, p, p, N, 0, N) == binding.TPR_ERR_WORKSPACE
+    assert b"workspace" in lib.tprank_last_error()
+
+
+def test_mlp_and_ce_reject_bad_arguments(lib):
+    g = lib.tp_mlp_fwd_bwd
+    assert g(1, 1, 0, -2, 4, 4, *[N] * 8, N, 0, N) == binding.TPR_ERR_SHAPE
+    assert g(0, 1, 0, 2, 4, 4, *[N] * 8, N, 0, N) == binding.TPR_ERR_PARTITION
+    assert g(1, 1, 5, 2, 4, 4, *[N] * 8, N, 0, N) == binding.TPR_ERR_DTYPE
+    assert g(1, 1, 0, 2, 4, 4, *[N] * 8, N, 0, N) == binding.TPR_ERR_NULLPTR
+    h = lib.vocab_parallel_ce_fwd_bwd
+    assert h(1, 1, 4, 8, N, N, N, N, N, N, 0, N) == binding.TPR_ERR_NULLPTR
+    p = ctypes.c_void_p(16)
+    assert h(1, 1, 4, 0, p, p, p, p, N, N, 0, N) == binding.TPR_ERR_SHAPE
+    assert h(0, 1, 4, 8, p, p, p, p, N, N, 0, N) == binding.TPR_ERR_PARTITION
+    assert h(2, 9, 4, 8, p, p, p, p, N, N, 0, N) == binding.TPR_ERR_DTYPE
+    assert h(2, 1, 4, 8, p, p, p, p, N, N, 0, N) == binding.TPR_ERR_WORKSPACE

@@ -176,3 +176,14 @@ def test_mlp_shape_errors():
         oracle.mlp_fwd_bwd(np.ones((2, 3)), np.ones((4, 5)), np.ones((5, 4)), np.ones((2, 3)))
     with pytest.raises(ValueError, match="partition"):
         oracle.tp_mlp_fwd_bwd(np.ones((2, 3)), np.ones((3, 5)), np.ones((5, 3)), np.ones((2, 3)), 0)
+
+
+def test_mlp_empty_feature_and_token_dims():
+    # zero tokens, zero hidden units or zero features: shapes are kept and empty
+    # contractions give exact zeros
+    for T, d, f in ((0, 3, 4), (5, 3, 0), (5, 0, 4)):
+        x, w1, w2, gy = np.ones((T, d)), np.ones((d, f)), np.ones((f, d)), np.ones((T, d))
+        y, dx, dw1, dw2 = oracle.mlp_fwd_bwd(x, w1, w2, gy)
+        assert y.shape == (T, d) and dx.shape == (T, d) and dw1.shape == (d, f) and dw2.shape == (f, d)
+        for t in (y, dx, dw1, dw2):
+            assert not t.any()
