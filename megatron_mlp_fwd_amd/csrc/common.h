@@ -43,6 +43,10 @@ enum Epilogue {
 // A group of problems sharing dtype, layout and epilogue.  Launchers return
 // hipSuccess or the launch error.
 hipError_t launch_gemm_bf16(GemmBatch& b, bool a_kmajor, bool b_kmajor, int epi, hipStream_t s);
+// Direct-to-LDS bf16 kernel (gemm_bf16_dma.hip), used by launch_gemm_bf16
+// when every problem of the group is eligible.
+bool gemm_bf16_dma_eligible(const GemmProb& p, bool a_kmajor, bool b_kmajor);
+hipError_t launch_gemm_bf16_dma(GemmBatch& b, bool a_kmajor, bool b_kmajor, int epi, int vec_c, hipStream_t s);
 hipError_t launch_gemm_f32(GemmBatch& b, bool a_kmajor, bool b_kmajor, int epi, hipStream_t s);
 
 // ---------------------------------------------------------------- reductions

@@ -21,49 +21,23 @@
 //
 // Grouped launch: up to kMaxGroup problems (one per simulated rank) share a
 // flattened grid; each block finds its problem by tile_start.
-#include "common.h"
+#include <cstdlib>
+#include <cstring>
+
+#include "gemm_common.h"
 
 namespace tpr {
 namespace {
 
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef float floatx4 __attribute__((ext_vector_type(4)));
-typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+using namespace gemm;
 
-constexpr int BM = 256, BN = 256, BK = 64;
-constexpr int NT = 256;
-constexpr int WTM = 128, WTN = 128;
-constexpr int FM = WTM / 16, FN = WTN / 16;
+constexpr int BK = 64;
 constexpr int STAGE = (BM + BN) * BK;  // bf16 elements per LDS stage
-constexpr int GROUP_M = 8;             // tile rows per raster group (L2 reuse of B)
 
 // 16-byte chunk swizzle of a k-contiguous LDS row (8 chunks per row); keeps
 // both the fragment reads and the row writes free of bank conflicts for 8- and
 // 16-lane LDS phases.
 __device__ __forceinline__ int swz(int row) { return (row & 7) ^ ((row >> 3) & 1); }
-
-__device__ __forceinline__ uint32_t pack_bf16(float a, float b) {
-  const uint32_t x = __builtin_bit_cast(uint16_t, (__bf16)a);
-  const uint32_t y = __builtin_bit_cast(uint16_t, (__bf16)b);
-  return x | (y << 16);
-}
-__device__ __forceinline__ float bf_lo(uint32_t w) { return __uint_as_float(w << 16); }
-__device__ __forceinline__ float bf_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
-
-// Exact-erf GELU and its derivative (fp32).  Phi(x) = erfc(-x/sqrt2)/2.
-__device__ __forceinline__ float gelu_f(float x) { return 0.5f * x * erfcf(-0.70710678118654752f * x); }
-__device__ __forceinline__ float gelu_prime_f(float x) {
-  return 0.5f * erfcf(-0.70710678118654752f * x) + 0.39894228040143268f * x * expf(-0.5f * x * x);
-}
-
-// Workgroups are handed to the 8 XCDs round-robin; renumber so that each XCD
-// walks a contiguous range of tiles (neighbouring tiles share L2 there).
-__device__ __forceinline__ int xcd_remap(int bid, int total) {
-  const int per = total >> 3, rem = total & 7;
-  const int x = bid & 7, slot = bid >> 3;
-  return x * per + (x < rem ? x : rem) + slot;
-}
 
 // Load one 64-deep k-slab of an operand with R rows (the M or N side) into
 // eight 16-byte registers.  Operand element (r, k) = X[r * s_r + k * s_k].
@@ -164,55 +138,6 @@ __device__ __forceinline__ void mma_stage(const uint16_t* __restrict__ As, const
   }
 }
 
-constexpr int EP_LD = WTN + 4;  // padded fp32 row of the epilogue staging area
-
-// Apply the epilogue to four consecutive outputs C[m][n .. n+3] (off = m*ldc+n).
-template <int EPI>
-__device__ __forceinline__ void epilogue_store(const GemmProb& P, floatx4 v, int64_t off, int n, int N, int vec_c) {
-  const bool full = vec_c && (n + 3 < N);
-  if constexpr (EPI == EPI_F32) {
-    float* c = static_cast<float*>(P.C) + off;
-    if (full) {
-      *reinterpret_cast<floatx4*>(c) = v;
-    } else {
-      for (int r = 0; r < 4; ++r)
-        if (n + r < N) c[r] = v[r];
-    }
-  } else if constexpr (EPI == EPI_GELU) {
-    uint16_t* c = static_cast<uint16_t*>(P.C) + off;
-    uint16_t* h = static_cast<uint16_t*>(P.aux_out) + off;
-    floatx4 gv;
-    for (int r = 0; r < 4; ++r) gv[r] = gelu_f(v[r]);
-    if (full) {
-      *reinterpret_cast<u32x2*>(c) = u32x2{pack_bf16(v[0], v[1]), pack_bf16(v[2], v[3])};
-      *reinterpret_cast<u32x2*>(h) = u32x2{pack_bf16(gv[0], gv[1]), pack_bf16(gv[2], gv[3])};
-    } else {
-      for (int r = 0; r < 4; ++r)
-        if (n + r < N) {
-          c[r] = __builtin_bit_cast(uint16_t, (__bf16)v[r]);
-          h[r] = __builtin_bit_cast(uint16_t, (__bf16)gv[r]);
-        }
-    }
-  } else {  // EPI_DGELU: C = acc * gelu'(pre), pre read from aux_in (may alias C)
-    const uint16_t* p = static_cast<const uint16_t*>(P.aux_in) + off;
-    uint16_t* c = static_cast<uint16_t*>(P.C) + off;
-    if (full) {
-      const u32x2 pw = *reinterpret_cast<const u32x2*>(p);
-      v[0] *= gelu_prime_f(bf_lo(pw[0]));
-      v[1] *= gelu_prime_f(bf_hi(pw[0]));
-      v[2] *= gelu_prime_f(bf_lo(pw[1]));
-      v[3] *= gelu_prime_f(bf_hi(pw[1]));
-      *reinterpret_cast<u32x2*>(c) = u32x2{pack_bf16(v[0], v[1]), pack_bf16(v[2], v[3])};
-    } else {
-      for (int r = 0; r < 4; ++r)
-        if (n + r < N) {
-          const float pre = __uint_as_float((uint32_t)p[r] << 16);
-          c[r] = __builtin_bit_cast(uint16_t, (__bf16)(v[r] * gelu_prime_f(pre)));
-        }
-    }
-  }
-}
-
 template <bool AK, bool BKM, bool VEC, int EPI>
 __global__ __launch_bounds__(NT, 1) void gemm_bf16_kernel(const GemmBatch batch, int vec_c) {
   __shared__ __attribute__((aligned(16))) uint16_t smem[2 * STAGE];
@@ -220,22 +145,10 @@ __global__ __launch_bounds__(NT, 1) void gemm_bf16_kernel(const GemmBatch batch,
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
   const int wm = wid >> 1, wn = wid & 1;
 
-  const int bid = xcd_remap((int)blockIdx.x, batch.total_tiles);
-  int g = 0;
-#pragma unroll
-  for (int i = 1; i < kMaxGroup; ++i)
-    if (i < batch.count && bid >= batch.p[i].tile_start) g = i;
-  const GemmProb& P = batch.p[g];
+  const TileCoord tc = locate_tile(batch);
+  const GemmProb& P = batch.p[tc.g];
   const int M = P.M, N = P.N, K = P.K;
-
-  int local = bid - P.tile_start;
-  const int per_group = GROUP_M * P.tiles_n;
-  const int first_m = (local / per_group) * GROUP_M;
-  const int gsize = min(P.tiles_m - first_m, GROUP_M);
-  local %= per_group;
-  const int tm = first_m + local % gsize;
-  const int tn = local / gsize;
-  const int m0 = tm * BM, n0 = tn * BN;
+  const int m0 = tc.tm * BM, n0 = tc.tn * BN;
 
   const uint16_t* __restrict__ A = static_cast<const uint16_t*>(P.A);
   const uint16_t* __restrict__ B = static_cast<const uint16_t*>(P.B);
@@ -271,33 +184,7 @@ __global__ __launch_bounds__(NT, 1) void gemm_bf16_kernel(const GemmBatch batch,
     __syncthreads();
   }
 
-  // Epilogue, in four passes through LDS (the operand stages are free now):
-  // pass q moves MFMA blocks mi = 2q, 2q+1 of every wave (a 32 x 128 region
-  // per wave) into LDS, then each wave reads its region back row-contiguously
-  // (32 lanes x 16 B per row) and applies the epilogue with coalesced stores.
-  float* ep = reinterpret_cast<float*>(smem) + wid * (32 * EP_LD);
-  const int64_t ldc = P.ldc;
-#pragma unroll
-  for (int q = 0; q < FM / 2; ++q) {
-#pragma unroll
-    for (int h = 0; h < 2; ++h)
-#pragma unroll
-      for (int ni = 0; ni < FN; ++ni)
-        *reinterpret_cast<floatx4*>(ep + (h * 16 + (lane & 15)) * EP_LD + ni * 16 + 4 * (lane >> 4)) =
-            acc[ni][2 * q + h];
-    __syncthreads();
-    const int col = 4 * (lane & 31);
-    const int n = n0 + wn * WTN + col;
-    for (int it = 0; it < 16; ++it) {
-      const int row = 2 * it + (lane >> 5);
-      const int m = m0 + wm * WTM + 32 * q + row;
-      if (m < M && n < N) {
-        floatx4 v = *reinterpret_cast<const floatx4*>(ep + row * EP_LD + col);
-        epilogue_store<EPI>(P, v, (int64_t)m * ldc + n, n, N, vec_c);
-      }
-    }
-    __syncthreads();
-  }
+  epilogue_via_lds<EPI, WTM, WTN>(reinterpret_cast<float*>(smem), acc, P, m0, n0, wid, wm, wn, lane, vec_c);
 }
 
 template <bool AK, bool BKM, bool VEC>
@@ -317,7 +204,7 @@ bool aligned(const void* p, int bytes) { return (reinterpret_cast<uintptr_t>(p) 
 
 hipError_t launch_gemm_bf16(GemmBatch& b, bool a_kmajor, bool b_kmajor, int epi, hipStream_t s) {
   int total = 0;
-  bool vec = true, vec_c = true;
+  bool vec = true, vec_c = true, dma = true;
   for (int i = 0; i < b.count; ++i) {
     GemmProb& p = b.p[i];
     p.tiles_m = (p.M + BM - 1) / BM;
@@ -330,6 +217,7 @@ hipError_t launch_gemm_bf16(GemmBatch& b, bool a_kmajor, bool b_kmajor, int epi,
     const int a_ext = a_kmajor ? p.K : p.M, b_ext = b_kmajor ? p.K : p.N;
     vec = vec && aligned(p.A, 16) && aligned(p.B, 16) && a_ld % 8 == 0 && b_ld % 8 == 0 && a_ext % 8 == 0 &&
           b_ext % 8 == 0;
+    dma = dma && gemm_bf16_dma_eligible(p, a_kmajor, b_kmajor);
     const int cbytes = epi == EPI_F32 ? 16 : 8;
     vec_c = vec_c && aligned(p.C, cbytes) && p.ldc % 4 == 0 && (epi != EPI_GELU || aligned(p.aux_out, 8)) &&
             (epi != EPI_DGELU || aligned(p.aux_in, 8));
@@ -337,6 +225,11 @@ hipError_t launch_gemm_bf16(GemmBatch& b, bool a_kmajor, bool b_kmajor, int epi,
   b.total_tiles = total;
   if (total == 0) return hipSuccess;
   const int vc = vec_c ? 1 : 0;
+  // TPRANK_GEMM_PATH=staged forces the register-staged kernel (used by tests
+  // to cover it on shapes the direct-to-LDS kernel would take).
+  const char* path = getenv("TPRANK_GEMM_PATH");
+  if (dma && !(path != nullptr && strcmp(path, "staged") == 0))
+    return launch_gemm_bf16_dma(b, a_kmajor, b_kmajor, epi, vc, s);
   if (a_kmajor && !b_kmajor) return vec ? launch_epi<true, false, true>(b, epi, vc, s) : launch_epi<true, false, false>(b, epi, vc, s);
   if (a_kmajor && b_kmajor) return vec ? launch_epi<true, true, true>(b, epi, vc, s) : launch_epi<true, true, false>(b, epi, vc, s);
   if (!a_kmajor && !b_kmajor) return vec ? launch_epi<false, false, true>(b, epi, vc, s) : launch_epi<false, false, false>(b, epi, vc, s);

@@ -111,14 +111,26 @@ def test_zero_sizes(tpr, axis, shape, dtype):
         np.testing.assert_array_equal(f64(o), w)  # empty contractions give exact zeros
 
 
-BF16_GEMM_SHAPES = [(512, 256, 512), (300, 136, 520), (264, 72, 40), (1000, 1000, 24), (7, 9, 11)]
+BF16_GEMM_SHAPES = [(512, 256, 512), (300, 136, 520), (264, 72, 40), (1000, 1000, 24), (7, 9, 11), (520, 96, 264),
+                    (256, 1024, 768)]
+
+
+@pytest.fixture(params=["auto", "staged"])
+def gemm_path(request, monkeypatch):
+    # "auto" lets the library pick the direct-to-LDS kernel where eligible;
+    # "staged" forces the register-staged kernel on the same shapes.
+    if request.param == "staged":
+        monkeypatch.setenv("TPRANK_GEMM_PATH", "staged")
+    else:
+        monkeypatch.delenv("TPRANK_GEMM_PATH", raising=False)
+    return request.param
 
 
 @pytest.mark.parametrize("parts", [1, 3, 8])
 @pytest.mark.parametrize("shape", BF16_GEMM_SHAPES)
 @pytest.mark.parametrize("axis", ["rows", "columns", "inner"])
-def test_bf16_gemm_tiles_and_tails(tpr, axis, shape, parts):
-    say("bf16 sharded GEMM", axis, shape, parts)
+def test_bf16_gemm_tiles_and_tails(tpr, axis, shape, parts, gemm_path):
+    say("bf16 sharded GEMM", axis, shape, parts, gemm_path)
     M, K, N = shape
     a, b, g = workloads.inner_gemm(M, K, N, seed=M + K + N + parts, device=DEV, b_std=1.0)
     got = tpr.sharded_matmul_fwd_bwd(axis, parts, a, b, g)
@@ -195,9 +207,9 @@ def test_mlp_fp32_uneven_and_empty_ranks(tpr, tp, layout):
 
 @pytest.mark.parametrize("layout", ["math", "torch"])
 @pytest.mark.parametrize("tp", [1, 2, 3])
-@pytest.mark.parametrize("shape", [(512, 256, 256), (300, 264, 200), (64, 40, 24)])
-def test_mlp_bf16_tiles_and_tails(tpr, shape, tp, layout):
-    say("TP MLP bf16", shape, tp, layout)
+@pytest.mark.parametrize("shape", [(512, 256, 256), (300, 264, 200), (64, 40, 24), (96, 512, 768)])
+def test_mlp_bf16_tiles_and_tails(tpr, shape, tp, layout, gemm_path):
+    say("TP MLP bf16", shape, tp, layout, gemm_path)
     T, d, f = shape
     x, w1, w2, gy = workloads.rank_mlp(T, d, f, seed=T + tp, device=DEV, w_std=0.05)
     if layout == "torch":
