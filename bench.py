@@ -14,7 +14,7 @@ GB/s (2 bytes read + 2 bytes written per logit) and the inner GEMM's TFLOP/s
 are reported beside it.  Each call is timed with HIP events on the stream the
 library launches on.
 
-Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline] [--copy-bytes N]
 """
 import argparse
 import hashlib
@@ -96,6 +96,9 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-bytes", type=int, default=0,
+                    help="also run one plain copy kernel (torch.neg on fp32) of this many bytes before timing, "
+                         "so that profiler byte counters can be calibrated against a known size")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: every simulated tensor-parallel rank runs on that device. "
@@ -123,6 +126,13 @@ def main():
     ce_out = (torch.empty((), device=dev), torch.empty_like(logits), None)
     ce_ws = torch.empty(tpr.vocab_parallel_ce_workspace_bytes(CE["parts"], CE["T"], CE["V"]), dtype=torch.uint8,
                         device=dev)
+
+    if args.copy_bytes > 0:
+        src = torch.ones(args.copy_bytes // 4, device=dev)
+        dst = torch.empty_like(src)
+        torch.neg(src, out=dst)
+        torch.cuda.synchronize()
+        del src, dst
 
     def step(ev):
         ev[0].record()

@@ -45,6 +45,17 @@ typedef short shortx4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) shortx4 lds_shortx4;
 typedef __attribute__((address_space(3))) bf16x8 lds_bf16x8;
 
+// A fragment is held as two 64-bit halves until it is consumed: the transpose
+// reads (inline assembly) write each half directly, and the halves are only
+// combined into the MFMA's 128-bit operand after the lgkmcnt wait that covers
+// them, so no register copy can ever read a half before its data has landed.
+struct Frag {
+  u32x2 lo, hi;
+};
+__device__ __forceinline__ bf16x8 as_operand(const Frag& f) {
+  return __builtin_bit_cast(bf16x8, u32x4{f.lo[0], f.lo[1], f.hi[0], f.hi[1]});
+}
+
 __device__ __forceinline__ int kswz(int rr) { return ((rr >> 1) & 3) ^ (((rr >> 3) & 1) * 3); }
 __device__ __forceinline__ int mswz(int k) { return (2 * (k & 3)) ^ (8 * ((k >> 3) & 1)); }
 
@@ -98,6 +109,11 @@ __device__ __forceinline__ void dma_issue(const DmaOperand& d, lds_u8* tile, int
                                              d.voff[j], soff, 0, 0);
 }
 
+__device__ __forceinline__ void dma_one(const DmaOperand& d, lds_u8* dst, int j, uint32_t soff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(d.rsrc, (__attribute__((address_space(3))) void*)dst, 16, d.voff[j], soff,
+                                           0, 0);
+}
+
 // Per-lane LDS byte offsets of the NF fragments (rows row0 + 16 f .. +15) a
 // wave reads from one tile.
 template <bool KMAJ, int NF>
@@ -120,49 +136,56 @@ __device__ __forceinline__ void frag_offsets(uint32_t (&off)[NF], int row0, int 
 // and 8G+4..8G+7 of the lane's row).  Issued as inline assembly because the
 // compiler places a wait for every outstanding LDS DMA in front of the builtin
 // form, which would drain the stage ring each slab; the caller therefore waits
-// on lgkmcnt itself (tr_wait) before the fragments are used.
-__device__ __forceinline__ bf16x8 ds_read_tr_frag(uint32_t addr) {
-  u32x2 lo, hi;
+// on lgkmcnt itself (frag_wait) before the fragments are used.
+__device__ __forceinline__ Frag ds_read_tr_frag(uint32_t addr) {
+  Frag f;
   asm volatile("ds_read_b64_tr_b16 %0, %2\n\tds_read_b64_tr_b16 %1, %2 offset:2048"
-               : "=&v"(lo), "=&v"(hi)
+               : "=&v"(f.lo), "=&v"(f.hi)
                : "v"(addr));
-  const u32x4 r = {lo[0], lo[1], hi[0], hi[1]};
-  return __builtin_bit_cast(bf16x8, r);
+  return f;
 }
 
-template <bool KMAJ, int NF>
-__device__ __forceinline__ void read_frags(bf16x8 (&fr)[NF], const lds_u8* tile, const uint32_t (&off)[NF]) {
-#pragma unroll
-  for (int f = 0; f < NF; ++f) {
-    if constexpr (KMAJ) {
-      fr[f] = *reinterpret_cast<const lds_bf16x8*>(tile + off[f]);
-    } else {
-      fr[f] = ds_read_tr_frag((uint32_t)(uintptr_t)(tile + off[f]));
-    }
+template <bool KMAJ>
+__device__ __forceinline__ Frag read_frag(const lds_u8* tile, uint32_t off) {
+  if constexpr (KMAJ) {
+    const u32x4 v = *reinterpret_cast<const __attribute__((address_space(3))) u32x4*>(tile + off);
+    return Frag{u32x2{v[0], v[1]}, u32x2{v[2], v[3]}};
+  } else {
+    return ds_read_tr_frag((uint32_t)(uintptr_t)(tile + off));
   }
 }
 
-// Wait for this wave's outstanding LDS reads and make the fragments depend on
-// the wait, so no MFMA that reads them can be scheduled above it.
+template <bool KMAJ, int NF>
+__device__ __forceinline__ void read_frags(Frag (&fr)[NF], const lds_u8* tile, const uint32_t (&off)[NF]) {
+#pragma unroll
+  for (int f = 0; f < NF; ++f) fr[f] = read_frag<KMAJ>(tile, off[f]);
+}
+
+// Wait for this wave's outstanding LDS reads and make both halves of every
+// fragment depend on the wait, so nothing that reads them (MFMA operand
+// assembly included) can be scheduled above it.
 template <int NF>
-__device__ __forceinline__ void tr_wait(bf16x8 (&fr)[NF]) {
+__device__ __forceinline__ void frag_wait(Frag (&fr)[NF]) {
   static_assert(NF == 4 || NF == 8, "fragment count");
   if constexpr (NF == 4) {
-    asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(fr[0]), "+v"(fr[1]), "+v"(fr[2]), "+v"(fr[3]));
+    asm volatile("s_waitcnt lgkmcnt(0)"
+                 : "+v"(fr[0].lo), "+v"(fr[0].hi), "+v"(fr[1].lo), "+v"(fr[1].hi), "+v"(fr[2].lo), "+v"(fr[2].hi),
+                   "+v"(fr[3].lo), "+v"(fr[3].hi));
   } else {
     asm volatile("s_waitcnt lgkmcnt(0)"
-                 : "+v"(fr[0]), "+v"(fr[1]), "+v"(fr[2]), "+v"(fr[3]), "+v"(fr[4]), "+v"(fr[5]), "+v"(fr[6]),
-                   "+v"(fr[7]));
+                 : "+v"(fr[0].lo), "+v"(fr[0].hi), "+v"(fr[1].lo), "+v"(fr[1].hi), "+v"(fr[2].lo), "+v"(fr[2].hi),
+                   "+v"(fr[3].lo), "+v"(fr[3].hi), "+v"(fr[4].lo), "+v"(fr[4].hi), "+v"(fr[5].lo), "+v"(fr[5].hi),
+                   "+v"(fr[6].lo), "+v"(fr[6].hi), "+v"(fr[7].lo), "+v"(fr[7].hi));
   }
 }
 
 template <int NI0>
-__device__ __forceinline__ void mma_half(floatx4 (&acc)[FN8][FM8], const bf16x8 (&a)[FM8], const bf16x8 (&b)[FN8]) {
+__device__ __forceinline__ void mma_half(floatx4 (&acc)[FN8][FM8], const Frag (&a)[FM8], const Frag (&b)[FN8]) {
 #pragma unroll
   for (int ni = NI0; ni < NI0 + FN8 / 2; ++ni)
 #pragma unroll
     for (int mi = 0; mi < FM8; ++mi)
-      acc[ni][mi] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(b[ni], a[mi], acc[ni][mi], 0, 0, 0);
+      acc[ni][mi] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_operand(b[ni]), as_operand(a[mi]), acc[ni][mi], 0, 0, 0);
 }
 
 template <bool AK, bool BKM, int EPI>
@@ -203,15 +226,20 @@ __global__ __launch_bounds__(NT8, 1) void gemm_bf16_dma_kernel(const GemmBatch b
     wait_vm_dyn(min(NS - 2, nk - 1) * LOADS_PER_STAGE);
     __builtin_amdgcn_s_barrier();
 
-    bf16x8 fa[2][FM8], fb[2][FN8];
+    Frag fa[2][FM8], fb[2][FN8];
     read_frags<AK, FM8>(fa[0], smem, aoff);
     read_frags<BKM, FN8>(fb[0], smem + TILE_BYTES, boff);
 
-    // One slab per step; the fragment register set alternates, so the loop
-    // body covers a pair of slabs.
-    auto step = [&](int kt, bf16x8(&ca)[FM8], bf16x8(&cb)[FN8], bf16x8(&na)[FM8], bf16x8(&nb)[FN8]) {
-      if constexpr (!AK) tr_wait<FM8>(ca);
-      if constexpr (!BKM) tr_wait<FN8>(cb);
+    // One slab per step; the fragment register sets alternate, so loops cover
+    // a pair of slabs.  `step` is the general form (any position, guarded);
+    // `steady` is the branch-free form used while every slab still has a
+    // successor to read and a slab to prefetch.  In `steady` the second half
+    // of the MFMAs is interleaved with the slab's 4 DMA issues and the next
+    // fragment reads, and scheduling fences keep the first half ahead of the
+    // barrier (the MFMAs carry no memory dependency the compiler could see).
+    auto step = [&](int kt, Frag(&ca)[FM8], Frag(&cb)[FN8], Frag(&na)[FM8], Frag(&nb)[FN8]) {
+      frag_wait<FM8>(ca);
+      frag_wait<FN8>(cb);
       mma_half<0>(acc, ca, cb);
       if (kt + 1 < nk) {
         wait_vm_dyn((min(kt + NS - 2, nk - 1) - (kt + 1)) * LOADS_PER_STAGE);
@@ -228,7 +256,49 @@ __global__ __launch_bounds__(NT8, 1) void gemm_bf16_dma_kernel(const GemmBatch b
       }
       mma_half<FN8 / 2>(acc, ca, cb);
     };
-    for (int kt = 0; kt < nk; kt += 2) {
+    auto steady = [&](int kt, Frag(&ca)[FM8], Frag(&cb)[FN8], Frag(&na)[FM8], Frag(&nb)[FN8]) {
+      frag_wait<FM8>(ca);
+      frag_wait<FN8>(cb);
+      mma_half<0>(acc, ca, cb);
+      __builtin_amdgcn_sched_barrier(0);
+      wait_vm<(NS - 3) * LOADS_PER_STAGE>();
+      __builtin_amdgcn_s_barrier();
+      __builtin_amdgcn_sched_barrier(0);
+      const int s_new = kt + NS - 1;
+      lds_u8* st = smem + (s_new % NS) * STAGE_BYTES;
+      const lds_u8* nx = smem + ((kt + 1) % NS) * STAGE_BYTES;
+      const uint32_t soa = (uint32_t)s_new * da.kstep, sob = (uint32_t)s_new * db.kstep;
+      lds_u8* dsta = st + wid * 2 * 1024;
+      lds_u8* dstb = st + TILE_BYTES + wid * 2 * 1024;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int ni = FN8 / 2 + i / FM8, mi = i % FM8;
+        acc[ni][mi] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_operand(cb[ni]), as_operand(ca[mi]), acc[ni][mi], 0, 0, 0);
+        if (i == 0) dma_one(da, dsta, 0, soa);
+        if (i == 2) dma_one(da, dsta + 1024, 1, soa);
+        if (i == 4) dma_one(db, dstb, 0, sob);
+        if (i == 6) dma_one(db, dstb + 1024, 1, sob);
+        if (i >= 1 && i < 1 + FM8) na[i - 1] = read_frag<AK>(nx, aoff[i - 1]);
+        if (i >= 1 + FM8 && i < 1 + FM8 + FN8) nb[i - 1 - FM8] = read_frag<BKM>(nx + TILE_BYTES, boff[i - 1 - FM8]);
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
+        __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);  // one VMEM (the DMA)
+      }
+#pragma unroll
+      for (int i = 0; i < 12; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // one LDS read
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    };
+    int kt = 0;
+    for (; kt + NS < nk; kt += 2) {
+      steady(kt, fa[0], fb[0], fa[1], fb[1]);
+      steady(kt + 1, fa[1], fb[1], fa[0], fb[0]);
+    }
+    for (; kt < nk; kt += 2) {
       step(kt, fa[0], fb[0], fa[1], fb[1]);
       if (kt + 1 < nk) step(kt + 1, fa[1], fb[1], fa[0], fb[0]);
     }
