@@ -2,7 +2,10 @@
 // shard planning, workspace carving and the launch sequence of each entry
 // point.  All validation happens before the first launch, so an error leaves
 // every output untouched.  Nothing here allocates device memory.
+#include <algorithm>
 #include <climits>
+#include <cstdlib>
+#include <cstring>
 #include <cstdarg>
 #include <cstdio>
 #include <string>
@@ -64,20 +67,56 @@ tpr::GemmProb prob(const void* A, int64_t sa_m, int64_t sa_k, const void* B, int
   return p;
 }
 
-// Run a list of same-layout problems as grouped launches of up to
-// kMaxGroup problems; problems with no output are dropped.
-hipError_t run_gemms(const std::vector<tpr::GemmProb>& ps, int dtype, bool a_kmajor, bool b_kmajor, int epi,
-                     hipStream_t s) {
-  std::vector<tpr::GemmProb> live;
-  for (const auto& p : ps)
-    if (p.M > 0 && p.N > 0) live.push_back(p);
-  for (size_t i = 0; i < live.size(); i += tpr::kMaxGroup) {
+// A GEMM to run: the problem plus its operand layouts and epilogue.
+struct Job {
+  tpr::GemmProb p;
+  bool ak, bk;
+  int epi;
+};
+
+Job job(const tpr::GemmProb& p, bool ak, bool bk, int epi) { return Job{p, ak, bk, epi}; }
+
+// Run a set of mutually independent GEMMs.  bf16 problems the direct-to-LDS
+// kernel accepts share heterogeneous launches (longest K first, so the
+// longest tiles are dispatched first and short ones fill in behind them);
+// everything else runs through the register-staged (bf16) or fp32 kernel,
+// grouped by layout and epilogue.  TPRANK_GEMM_PATH=staged sends every bf16
+// problem to the register-staged kernel (tests use it to cover that kernel).
+hipError_t run_jobs(std::vector<Job> jobs, int dtype, hipStream_t s) {
+  std::vector<Job> fast, rest;
+  const char* path = getenv("TPRANK_GEMM_PATH");
+  const bool staged_only = path != nullptr && strcmp(path, "staged") == 0;
+  for (const Job& j : jobs) {
+    if (j.p.M <= 0 || j.p.N <= 0) continue;
+    const bool dma = dtype == TPR_BF16 && !staged_only && tpr::gemm_bf16_dma_eligible(j.p, j.ak, j.bk, j.epi);
+    (dma ? fast : rest).push_back(j);
+  }
+  std::stable_sort(fast.begin(), fast.end(), [](const Job& x, const Job& y) { return x.p.K > y.p.K; });
+  for (size_t i = 0; i < fast.size(); i += tpr::kMaxGroup) {
     tpr::GemmBatch b{};
-    b.count = (int)std::min<size_t>(tpr::kMaxGroup, live.size() - i);
-    for (int j = 0; j < b.count; ++j) b.p[j] = live[i + j];
-    const hipError_t e = dtype == TPR_BF16 ? tpr::launch_gemm_bf16(b, a_kmajor, b_kmajor, epi, s)
-                                           : tpr::launch_gemm_f32(b, a_kmajor, b_kmajor, epi, s);
+    b.count = (int)std::min<size_t>(tpr::kMaxGroup, fast.size() - i);
+    for (int k = 0; k < b.count; ++k) {
+      const Job& j = fast[i + k];
+      b.p[k] = j.p;
+      b.p[k].kind = tpr::gemm_kind(j.ak, j.bk, j.epi);
+    }
+    const hipError_t e = tpr::launch_gemm_bf16_dma(b, s);
     if (e != hipSuccess) return e;
+  }
+  while (!rest.empty()) {
+    const Job head = rest.front();
+    std::vector<Job> same, other;
+    for (const Job& j : rest)
+      (j.ak == head.ak && j.bk == head.bk && j.epi == head.epi ? same : other).push_back(j);
+    for (size_t i = 0; i < same.size(); i += tpr::kMaxGroup) {
+      tpr::GemmBatch b{};
+      b.count = (int)std::min<size_t>(tpr::kMaxGroup, same.size() - i);
+      for (int k = 0; k < b.count; ++k) b.p[k] = same[i + k].p;
+      const hipError_t e = dtype == TPR_BF16 ? tpr::launch_gemm_bf16(b, head.ak, head.bk, head.epi, s)
+                                             : tpr::launch_gemm_f32(b, head.ak, head.bk, head.epi, s);
+      if (e != hipSuccess) return e;
+    }
+    rest.swap(other);
   }
   return hipSuccess;
 }
@@ -138,7 +177,7 @@ int sharded_matmul_fwd_bwd(int axis, int parts, int dtype, int64_t M, int64_t K,
   float* slots = static_cast<float*>(ws);
   const bool direct = parts == 1;
   int nslots = 0;
-  std::vector<tpr::GemmProb> fy, fda, fdb;
+  std::vector<Job> jobs;  // Y (NN), dA (NT) and dB (TN) of every rank are independent
 
   for (int r = 0; r < parts; ++r) {
     int64_t lo, hi;
@@ -147,20 +186,20 @@ int sharded_matmul_fwd_bwd(int axis, int parts, int dtype, int64_t M, int64_t K,
       const int64_t m = hi - lo;
       if (m == 0) continue;
       // Y_r = A_r B and dA_r = G_r B^T land in their row slices; dB_r = A_r^T G_r is a partial.
-      fy.push_back(prob(cb(A) + lo * K * e, K, 1, B, N, 1, Y + lo * N, N, m, N, K));
-      fda.push_back(prob(cb(G) + lo * N * e, N, 1, B, 1, N, dA + lo * K, K, m, K, N));
+      jobs.push_back(job(prob(cb(A) + lo * K * e, K, 1, B, N, 1, Y + lo * N, N, m, N, K), true, false, tpr::EPI_F32));
+      jobs.push_back(job(prob(cb(G) + lo * N * e, N, 1, B, 1, N, dA + lo * K, K, m, K, N), true, true, tpr::EPI_F32));
       float* dst = direct ? dB : slots + nslots * stride;
-      fdb.push_back(prob(cb(A) + lo * K * e, 1, K, cb(G) + lo * N * e, N, 1, dst, N, K, N, m));
+      jobs.push_back(job(prob(cb(A) + lo * K * e, 1, K, cb(G) + lo * N * e, N, 1, dst, N, K, N, m), false, false, tpr::EPI_F32));
       ++nslots;
     } else if (axis == TPR_COLUMNS) {
       shard_of(N, parts, r, &lo, &hi);
       const int64_t n = hi - lo;
       if (n == 0) continue;
       // Y_r = A B_r and dB_r = A^T G_r land in their column slices; dA_r = G_r B_r^T is a partial.
-      fy.push_back(prob(A, K, 1, cb(B) + lo * e, N, 1, Y + lo, N, M, n, K));
-      fdb.push_back(prob(A, 1, K, cb(G) + lo * e, N, 1, dB + lo, N, K, n, M));
+      jobs.push_back(job(prob(A, K, 1, cb(B) + lo * e, N, 1, Y + lo, N, M, n, K), true, false, tpr::EPI_F32));
+      jobs.push_back(job(prob(A, 1, K, cb(G) + lo * e, N, 1, dB + lo, N, K, n, M), false, false, tpr::EPI_F32));
       float* dst = direct ? dA : slots + nslots * stride;
-      fda.push_back(prob(cb(G) + lo * e, N, 1, cb(B) + lo * e, 1, N, dst, K, M, K, n));
+      jobs.push_back(job(prob(cb(G) + lo * e, N, 1, cb(B) + lo * e, 1, N, dst, K, M, K, n), true, true, tpr::EPI_F32));
       ++nslots;
     } else {
       shard_of(K, parts, r, &lo, &hi);
@@ -168,17 +207,15 @@ int sharded_matmul_fwd_bwd(int axis, int parts, int dtype, int64_t M, int64_t K,
       if (k == 0) continue;
       // Y_r = A_r B_r is a partial; dA_r = G B_r^T and dB_r = A_r^T G land in their K slices.
       float* dst = direct ? Y : slots + nslots * stride;
-      fy.push_back(prob(cb(A) + lo * e, K, 1, cb(B) + lo * N * e, N, 1, dst, N, M, N, k));
-      fda.push_back(prob(G, N, 1, cb(B) + lo * N * e, 1, N, dA + lo, K, M, k, N));
-      fdb.push_back(prob(cb(A) + lo * e, 1, K, G, N, 1, dB + lo * N, N, k, N, M));
+      jobs.push_back(job(prob(cb(A) + lo * e, K, 1, cb(B) + lo * N * e, N, 1, dst, N, M, N, k), true, false, tpr::EPI_F32));
+      jobs.push_back(job(prob(G, N, 1, cb(B) + lo * N * e, 1, N, dA + lo, K, M, k, N), true, true, tpr::EPI_F32));
+      jobs.push_back(job(prob(cb(A) + lo * e, 1, K, G, N, 1, dB + lo * N, N, k, N, M), false, false, tpr::EPI_F32));
       ++nslots;
     }
   }
 
   hipError_t he;
-  if ((he = run_gemms(fy, dtype, true, false, tpr::EPI_F32, s)) != hipSuccess) return hip_fail(he, "Y GEMM");
-  if ((he = run_gemms(fda, dtype, true, true, tpr::EPI_F32, s)) != hipSuccess) return hip_fail(he, "dA GEMM");
-  if ((he = run_gemms(fdb, dtype, false, false, tpr::EPI_F32, s)) != hipSuccess) return hip_fail(he, "dB GEMM");
+  if ((he = run_jobs(jobs, dtype, s)) != hipSuccess) return hip_fail(he, "sharded GEMM launch");
   if (axis == TPR_ROWS)
     he = finish_sum(dB, K, N, slots, nslots, stride, direct, s);
   else if (axis == TPR_COLUMNS)
@@ -224,7 +261,8 @@ int tp_mlp_fwd_bwd(int tp, int dtype, int w_layout, int64_t T, int64_t d, int64_
   const bool direct = tp == 1;
   const bool math = w_layout == TPR_W_MATH;
   int nslots = 0;
-  std::vector<tpr::GemmProb> f1, f2, gw2, gh, gw1, gx;
+  // Launch groups: fc1 | fc2, dW2, dH (independent of each other) | dW1, dx.
+  std::vector<Job> fwd1, mid, last;
 
   for (int r = 0; r < tp; ++r) {
     int64_t lo, hi;
@@ -236,33 +274,30 @@ int tp_mlp_fwd_bwd(int tp, int dtype, int w_layout, int64_t T, int64_t d, int64_
     float* ydst = direct ? y : zpart + nslots * pstride;
     float* xdst = direct ? dx : xpart + nslots * pstride;
     if (math) {  // w1 d x f, w2 f x d
-      f1.push_back(prob(x, d, 1, cb(w1) + lo * e, f, 1, Pr, fr, T, fr, d, nullptr, Hr));
-      f2.push_back(prob(Hr, fr, 1, cb(w2) + lo * d * e, d, 1, ydst, d, T, d, fr));
-      gw2.push_back(prob(Hr, 1, fr, gy, d, 1, dw2 + lo * d, d, fr, d, T));
-      gh.push_back(prob(gy, d, 1, cb(w2) + lo * d * e, 1, d, Pr, fr, T, fr, d, Pr));
-      gw1.push_back(prob(x, 1, d, Pr, fr, 1, dw1 + lo, f, d, fr, T));
-      gx.push_back(prob(Pr, fr, 1, cb(w1) + lo * e, 1, f, xdst, d, T, d, fr));
+      fwd1.push_back(job(prob(x, d, 1, cb(w1) + lo * e, f, 1, Pr, fr, T, fr, d, nullptr, Hr), true, false, tpr::EPI_GELU));
+      mid.push_back(job(prob(Hr, fr, 1, cb(w2) + lo * d * e, d, 1, ydst, d, T, d, fr), true, false, tpr::EPI_F32));
+      mid.push_back(job(prob(Hr, 1, fr, gy, d, 1, dw2 + lo * d, d, fr, d, T), false, false, tpr::EPI_F32));
+      mid.push_back(job(prob(gy, d, 1, cb(w2) + lo * d * e, 1, d, Pr, fr, T, fr, d, Pr), true, true, tpr::EPI_DGELU));
+      last.push_back(job(prob(x, 1, d, Pr, fr, 1, dw1 + lo, f, d, fr, T), false, false, tpr::EPI_F32));
+      last.push_back(job(prob(Pr, fr, 1, cb(w1) + lo * e, 1, f, xdst, d, T, d, fr), true, true, tpr::EPI_F32));
     } else {  // w1 (f, d), w2 (d, f)
-      f1.push_back(prob(x, d, 1, cb(w1) + lo * d * e, 1, d, Pr, fr, T, fr, d, nullptr, Hr));
-      f2.push_back(prob(Hr, fr, 1, cb(w2) + lo * e, 1, f, ydst, d, T, d, fr));
-      gw2.push_back(prob(gy, 1, d, Hr, fr, 1, dw2 + lo, f, d, fr, T));
-      gh.push_back(prob(gy, d, 1, cb(w2) + lo * e, f, 1, Pr, fr, T, fr, d, Pr));
-      gw1.push_back(prob(Pr, 1, fr, x, d, 1, dw1 + lo * d, d, fr, d, T));
-      gx.push_back(prob(Pr, fr, 1, cb(w1) + lo * d * e, d, 1, xdst, d, T, d, fr));
+      fwd1.push_back(job(prob(x, d, 1, cb(w1) + lo * d * e, 1, d, Pr, fr, T, fr, d, nullptr, Hr), true, true, tpr::EPI_GELU));
+      mid.push_back(job(prob(Hr, fr, 1, cb(w2) + lo * e, 1, f, ydst, d, T, d, fr), true, true, tpr::EPI_F32));
+      mid.push_back(job(prob(gy, 1, d, Hr, fr, 1, dw2 + lo, f, d, fr, T), false, false, tpr::EPI_F32));
+      mid.push_back(job(prob(gy, d, 1, cb(w2) + lo * e, f, 1, Pr, fr, T, fr, d, Pr), true, false, tpr::EPI_DGELU));
+      last.push_back(job(prob(Pr, 1, fr, x, d, 1, dw1 + lo * d, d, fr, d, T), false, false, tpr::EPI_F32));
+      last.push_back(job(prob(Pr, fr, 1, cb(w1) + lo * d * e, d, 1, xdst, d, T, d, fr), true, false, tpr::EPI_F32));
     }
     ++nslots;
   }
 
   hipError_t he;
-  // Forward: column-parallel GEMM with the GELU epilogue, then the row-parallel GEMM.
-  if ((he = run_gemms(f1, dtype, true, !math, tpr::EPI_GELU, s)) != hipSuccess) return hip_fail(he, "fc1 GEMM");
-  if ((he = run_gemms(f2, dtype, true, !math, tpr::EPI_F32, s)) != hipSuccess) return hip_fail(he, "fc2 GEMM");
-  // Backward: weight gradient of fc2, activation gradient with the GELU' epilogue,
-  // weight gradient of fc1, input gradient.
-  if ((he = run_gemms(gw2, dtype, false, false, tpr::EPI_F32, s)) != hipSuccess) return hip_fail(he, "dW2 GEMM");
-  if ((he = run_gemms(gh, dtype, true, math, tpr::EPI_DGELU, s)) != hipSuccess) return hip_fail(he, "dH GEMM");
-  if ((he = run_gemms(gw1, dtype, false, false, tpr::EPI_F32, s)) != hipSuccess) return hip_fail(he, "dW1 GEMM");
-  if ((he = run_gemms(gx, dtype, true, math, tpr::EPI_F32, s)) != hipSuccess) return hip_fail(he, "dx GEMM");
+  // Forward fc1 (column-parallel GEMM, GELU epilogue); then fc2 (row-parallel
+  // GEMM) together with the two backward products that need only H and gy:
+  // dW2 and the activation gradient with the GELU' epilogue; then dW1 and dx.
+  if ((he = run_jobs(fwd1, dtype, s)) != hipSuccess) return hip_fail(he, "fc1 GEMM");
+  if ((he = run_jobs(mid, dtype, s)) != hipSuccess) return hip_fail(he, "fc2 / dW2 / dH GEMMs");
+  if ((he = run_jobs(last, dtype, s)) != hipSuccess) return hip_fail(he, "dW1 / dx GEMMs");
   // The block's one reduction each way: y = sum_r Z_r, dx = sum_r dx_r.
   if ((he = finish_sum(y, T, d, zpart, nslots, pstride, direct, s)) != hipSuccess) return hip_fail(he, "y reduction");
   if ((he = finish_sum(dx, T, d, xpart, nslots, pstride, direct, s)) != hipSuccess)

@@ -22,11 +22,12 @@ struct GemmProb {
   void* aux_out;        // epilogue second output (activation for EPI_GELU)
   int64_t sa_m, sa_k, sb_k, sb_n, ldc;
   int M, N, K;
+  int kind;              // gemm_kind(a_kmajor, b_kmajor, epilogue) for heterogeneous launches
   int tiles_m, tiles_n;  // filled by the launcher
   int tile_start;        // first flattened block index of this problem
 };
 
-constexpr int kMaxGroup = 8;  // problems per grouped launch
+constexpr int kMaxGroup = 16;  // problems per grouped launch
 
 struct GemmBatch {
   GemmProb p[kMaxGroup];
@@ -40,13 +41,20 @@ enum Epilogue {
   EPI_DGELU = 2,  // C (compute dtype) = acc * gelu'(aux_in)    [in place allowed]
 };
 
-// A group of problems sharing dtype, layout and epilogue.  Launchers return
-// hipSuccess or the launch error.
+constexpr int gemm_kind(bool a_kmajor, bool b_kmajor, int epi) {
+  return (a_kmajor ? 1 : 0) | (b_kmajor ? 2 : 0) | (epi << 2);
+}
+
+// Register-staged bf16 kernel (gemm_bf16.hip): a group of problems sharing
+// layout and epilogue, any shape or alignment.  Launchers return hipSuccess
+// or the launch error.
 hipError_t launch_gemm_bf16(GemmBatch& b, bool a_kmajor, bool b_kmajor, int epi, hipStream_t s);
-// Direct-to-LDS bf16 kernel (gemm_bf16_dma.hip), used by launch_gemm_bf16
-// when every problem of the group is eligible.
-bool gemm_bf16_dma_eligible(const GemmProb& p, bool a_kmajor, bool b_kmajor);
-hipError_t launch_gemm_bf16_dma(GemmBatch& b, bool a_kmajor, bool b_kmajor, int epi, int vec_c, hipStream_t s);
+// Direct-to-LDS bf16 kernel (gemm_bf16_dma.hip): a group of independent
+// problems that may differ in layout and epilogue (GemmProb::kind), each of
+// them eligible.  Problems should be ordered by decreasing K so the longest
+// tiles are dispatched first.
+bool gemm_bf16_dma_eligible(const GemmProb& p, bool a_kmajor, bool b_kmajor, int epi);
+hipError_t launch_gemm_bf16_dma(GemmBatch& b, hipStream_t s);
 hipError_t launch_gemm_f32(GemmBatch& b, bool a_kmajor, bool b_kmajor, int epi, hipStream_t s);
 
 // ---------------------------------------------------------------- reductions

@@ -21,9 +21,6 @@
 //
 // Grouped launch: up to kMaxGroup problems (one per simulated rank) share a
 // flattened grid; each block finds its problem by tile_start.
-#include <cstdlib>
-#include <cstring>
-
 #include "gemm_common.h"
 
 namespace tpr {
@@ -204,7 +201,7 @@ bool aligned(const void* p, int bytes) { return (reinterpret_cast<uintptr_t>(p) 
 
 hipError_t launch_gemm_bf16(GemmBatch& b, bool a_kmajor, bool b_kmajor, int epi, hipStream_t s) {
   int total = 0;
-  bool vec = true, vec_c = true, dma = true;
+  bool vec = true, vec_c = true;
   for (int i = 0; i < b.count; ++i) {
     GemmProb& p = b.p[i];
     p.tiles_m = (p.M + BM - 1) / BM;
@@ -217,7 +214,6 @@ hipError_t launch_gemm_bf16(GemmBatch& b, bool a_kmajor, bool b_kmajor, int epi,
     const int a_ext = a_kmajor ? p.K : p.M, b_ext = b_kmajor ? p.K : p.N;
     vec = vec && aligned(p.A, 16) && aligned(p.B, 16) && a_ld % 8 == 0 && b_ld % 8 == 0 && a_ext % 8 == 0 &&
           b_ext % 8 == 0;
-    dma = dma && gemm_bf16_dma_eligible(p, a_kmajor, b_kmajor);
     const int cbytes = epi == EPI_F32 ? 16 : 8;
     vec_c = vec_c && aligned(p.C, cbytes) && p.ldc % 4 == 0 && (epi != EPI_GELU || aligned(p.aux_out, 8)) &&
             (epi != EPI_DGELU || aligned(p.aux_in, 8));
@@ -225,11 +221,6 @@ hipError_t launch_gemm_bf16(GemmBatch& b, bool a_kmajor, bool b_kmajor, int epi,
   b.total_tiles = total;
   if (total == 0) return hipSuccess;
   const int vc = vec_c ? 1 : 0;
-  // TPRANK_GEMM_PATH=staged forces the register-staged kernel (used by tests
-  // to cover it on shapes the direct-to-LDS kernel would take).
-  const char* path = getenv("TPRANK_GEMM_PATH");
-  if (dma && !(path != nullptr && strcmp(path, "staged") == 0))
-    return launch_gemm_bf16_dma(b, a_kmajor, b_kmajor, epi, vc, s);
   if (a_kmajor && !b_kmajor) return vec ? launch_epi<true, false, true>(b, epi, vc, s) : launch_epi<true, false, false>(b, epi, vc, s);
   if (a_kmajor && b_kmajor) return vec ? launch_epi<true, true, true>(b, epi, vc, s) : launch_epi<true, true, false>(b, epi, vc, s);
   if (!a_kmajor && !b_kmajor) return vec ? launch_epi<false, false, true>(b, epi, vc, s) : launch_epi<false, false, false>(b, epi, vc, s);

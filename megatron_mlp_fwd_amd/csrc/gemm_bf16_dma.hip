@@ -188,18 +188,16 @@ __device__ __forceinline__ void mma_half(floatx4 (&acc)[FN8][FM8], const Frag (&
       acc[ni][mi] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_operand(b[ni]), as_operand(a[mi]), acc[ni][mi], 0, 0, 0);
 }
 
+// One 256 x 256 output tile of problem P.
 template <bool AK, bool BKM, int EPI>
-__global__ __launch_bounds__(NT8, 1) void gemm_bf16_dma_kernel(const GemmBatch batch, int vec_c) {
-  __shared__ __attribute__((aligned(1024))) uint8_t smem_raw[NS * STAGE_BYTES];
+__device__ __forceinline__ void gemm_tile(const GemmProb& P, int tm, int tn, uint8_t* smem_raw, int vec_c) {
   lds_u8* smem = (lds_u8*)smem_raw;
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wid >> 2, wn = wid & 3;
-  const TileCoord tc = locate_tile(batch);
-  const GemmProb& P = batch.p[tc.g];
   const int M = P.M, N = P.N, K = P.K;
-  const int m0 = tc.tm * BM, n0 = tc.tn * BN;
+  const int m0 = tm * BM, n0 = tn * BN;
 
   DmaOperand da, db;
   dma_setup<AK>(da, P.A, AK ? P.sa_m : P.sa_k, M, K, m0, wid, lane);
@@ -307,15 +305,40 @@ __global__ __launch_bounds__(NT8, 1) void gemm_bf16_dma_kernel(const GemmBatch b
   epilogue_via_lds<EPI, TM8, TN8>(reinterpret_cast<float*>(smem_raw), acc, P, m0, n0, wid, wm, wn, lane, vec_c);
 }
 
-template <bool AK, bool BKM>
-hipError_t launch_epi(const GemmBatch& b, int epi, int vec_c, hipStream_t s) {
-  const dim3 grid(b.total_tiles), block(NT8);
-  switch (epi) {
-    case EPI_F32: hipLaunchKernelGGL((gemm_bf16_dma_kernel<AK, BKM, EPI_F32>), grid, block, 0, s, b, vec_c); break;
-    case EPI_GELU: hipLaunchKernelGGL((gemm_bf16_dma_kernel<AK, BKM, EPI_GELU>), grid, block, 0, s, b, vec_c); break;
-    default: hipLaunchKernelGGL((gemm_bf16_dma_kernel<AK, BKM, EPI_DGELU>), grid, block, 0, s, b, vec_c); break;
+// Block -> (problem, tile).  Every problem's tiles start at a multiple of 8
+// blocks (padding blocks exit), so a block's XCD (blockIdx % 8, the hardware's
+// round-robin) is its position within the problem modulo 8; each XCD gets one
+// contiguous run of the problem's tiles, walked in grouped raster order.
+__global__ __launch_bounds__(NT8, 1) void gemm_bf16_dma_kernel(const GemmBatch batch) {
+  __shared__ __attribute__((aligned(1024))) uint8_t smem_raw[NS * STAGE_BYTES];
+  const int bid = blockIdx.x;
+  int g = 0;
+#pragma unroll
+  for (int i = 1; i < kMaxGroup; ++i)
+    if (i < batch.count && bid >= batch.p[i].tile_start) g = i;
+  const GemmProb& P = batch.p[g];
+  const int ntiles = P.tiles_m * P.tiles_n;
+  const int l = bid - P.tile_start;
+  const int per_xcd = (ntiles + 7) >> 3;
+  int local = (l & 7) * per_xcd + (l >> 3);
+  if (local >= ntiles) return;
+  const int per_group = GROUP_M * P.tiles_n;
+  const int first_m = (local / per_group) * GROUP_M;
+  const int gsize = min(P.tiles_m - first_m, GROUP_M);
+  local %= per_group;
+  const int tm = first_m + local % gsize, tn = local / gsize;
+  const int vec_c = P.kind >> 8;
+  switch (P.kind & 0xff) {
+    case gemm_kind(true, false, EPI_F32): gemm_tile<true, false, EPI_F32>(P, tm, tn, smem_raw, vec_c); break;
+    case gemm_kind(true, true, EPI_F32): gemm_tile<true, true, EPI_F32>(P, tm, tn, smem_raw, vec_c); break;
+    case gemm_kind(false, false, EPI_F32): gemm_tile<false, false, EPI_F32>(P, tm, tn, smem_raw, vec_c); break;
+    case gemm_kind(false, true, EPI_F32): gemm_tile<false, true, EPI_F32>(P, tm, tn, smem_raw, vec_c); break;
+    case gemm_kind(true, false, EPI_GELU): gemm_tile<true, false, EPI_GELU>(P, tm, tn, smem_raw, vec_c); break;
+    case gemm_kind(true, true, EPI_GELU): gemm_tile<true, true, EPI_GELU>(P, tm, tn, smem_raw, vec_c); break;
+    case gemm_kind(true, false, EPI_DGELU): gemm_tile<true, false, EPI_DGELU>(P, tm, tn, smem_raw, vec_c); break;
+    case gemm_kind(true, true, EPI_DGELU): gemm_tile<true, true, EPI_DGELU>(P, tm, tn, smem_raw, vec_c); break;
+    default: break;  // layouts the library never issues with these epilogues
   }
-  return hipGetLastError();
 }
 
 bool aligned(const void* p, int bytes) { return (reinterpret_cast<uintptr_t>(p) % bytes) == 0; }
@@ -324,10 +347,12 @@ bool aligned(const void* p, int bytes) { return (reinterpret_cast<uintptr_t>(p) 
 
 // Eligibility of a problem for the direct-to-LDS kernel: K a multiple of the
 // 32-deep slab, 16-byte aligned rows along each operand's contiguous
-// dimension, an extent along it that is a multiple of 8 elements, and
-// operand byte ranges that the 32-bit buffer offsets can address.
-bool gemm_bf16_dma_eligible(const GemmProb& p, bool a_kmajor, bool b_kmajor) {
+// dimension, an extent along it that is a multiple of 8 elements, operand byte
+// ranges that the 32-bit buffer offsets can address, and a (layout, epilogue)
+// pair the kernel instantiates (the GELU epilogues need a k-major A).
+bool gemm_bf16_dma_eligible(const GemmProb& p, bool a_kmajor, bool b_kmajor, int epi) {
   if (p.M <= 0 || p.N <= 0 || p.K <= 0 || p.K % BK != 0) return false;
+  if (epi != EPI_F32 && !a_kmajor) return false;
   const int64_t a_ld = a_kmajor ? p.sa_m : p.sa_k, b_ld = b_kmajor ? p.sb_n : p.sb_k;
   if ((a_kmajor ? p.sa_k : p.sa_m) != 1 || (b_kmajor ? p.sb_k : p.sb_n) != 1) return false;
   const int a_ext = a_kmajor ? p.K : p.M, b_ext = b_kmajor ? p.K : p.N;
@@ -338,11 +363,27 @@ bool gemm_bf16_dma_eligible(const GemmProb& p, bool a_kmajor, bool b_kmajor) {
   return a_bytes < limit && b_bytes < limit;
 }
 
-hipError_t launch_gemm_bf16_dma(GemmBatch& b, bool a_kmajor, bool b_kmajor, int epi, int vec_c, hipStream_t s) {
-  if (a_kmajor && !b_kmajor) return launch_epi<true, false>(b, epi, vec_c, s);
-  if (a_kmajor && b_kmajor) return launch_epi<true, true>(b, epi, vec_c, s);
-  if (!a_kmajor && !b_kmajor) return launch_epi<false, false>(b, epi, vec_c, s);
-  return launch_epi<false, true>(b, epi, vec_c, s);
+// Problems arrive with `kind` set; the launcher lays out the flattened grid
+// (each problem padded to a multiple of 8 blocks) and records whether each
+// problem's outputs allow vector stores (kind bit 8).
+hipError_t launch_gemm_bf16_dma(GemmBatch& b, hipStream_t s) {
+  int total = 0;
+  for (int i = 0; i < b.count; ++i) {
+    GemmProb& p = b.p[i];
+    const int epi = (p.kind >> 2) & 3;
+    p.tiles_m = (p.M + BM - 1) / BM;
+    p.tiles_n = (p.N + BN - 1) / BN;
+    p.tile_start = total;
+    total += ((p.tiles_m * p.tiles_n + 7) / 8) * 8;
+    const int cbytes = epi == EPI_F32 ? 16 : 8;
+    const bool vec_c = aligned(p.C, cbytes) && p.ldc % 4 == 0 && (epi != EPI_GELU || aligned(p.aux_out, 8)) &&
+                       (epi != EPI_DGELU || aligned(p.aux_in, 8));
+    p.kind = (p.kind & 0xff) | (vec_c ? 0x100 : 0);
+  }
+  b.total_tiles = total;
+  if (total == 0) return hipSuccess;
+  hipLaunchKernelGGL(gemm_bf16_dma_kernel, dim3(total), dim3(NT8), 0, s, b);
+  return hipGetLastError();
 }
 
 }  // namespace tpr
