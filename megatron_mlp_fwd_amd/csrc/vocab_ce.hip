@@ -13,7 +13,10 @@
 // one 1024-thread workgroup per row holds the whole row in registers (16
 // slots of 16 bytes per thread; a slot is a 1024-vector run inside one
 // shard), so the logits are read from HBM once and dlogits written once --
-// the kernel is bound by HBM bandwidth (4 bytes per logit).  Per-shard
+// the kernel is bound by HBM bandwidth (4 bytes per logit).  Each exponential
+// is computed once: the sum pass keeps exp(z - m) in place of the logit as
+// fp16 for the gradient pass (round-to-nearest; only terms below 2^-24 of the
+// row maximum flush to zero, which is far below bf16 output resolution).  Per-shard
 // statistics are reduced per wave (shuffles) and across waves in LDS in a
 // fixed order; the cross-shard combine ("all-reduce" of max, then of the
 // sums) is a loop over the shard slots in rank order.
@@ -46,15 +49,32 @@ struct CeSlots {
   int64_t sbeg[CE_PMAX + 1];
 };
 
+// Wave-wide reductions with DPP lane moves (no LDS traffic): swap neighbours,
+// pairs, half-rows and rows of 16, then broadcast row 0 into row 1 and rows
+// 0-1 into rows 2-3; lane 63 ends with the total, read back as a scalar.
+// Lanes a move does not feed keep the identity `id`.
+#define TPR_DPP(v, id, ctrl, rmask)                                                                           \
+  __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(__builtin_bit_cast(int, id), __builtin_bit_cast(int, v), \
+                                                        ctrl, rmask, 0xf, false))
 __device__ __forceinline__ float wave_max(float v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
-  return v;
+  const float id = -INFINITY;
+  v = fmaxf(v, TPR_DPP(v, id, 0xB1, 0xf));   // quad_perm [1,0,3,2]
+  v = fmaxf(v, TPR_DPP(v, id, 0x4E, 0xf));   // quad_perm [2,3,0,1]
+  v = fmaxf(v, TPR_DPP(v, id, 0x141, 0xf));  // row_half_mirror
+  v = fmaxf(v, TPR_DPP(v, id, 0x140, 0xf));  // row_mirror
+  v = fmaxf(v, TPR_DPP(v, id, 0x142, 0xa));  // row_bcast:15
+  v = fmaxf(v, TPR_DPP(v, id, 0x143, 0xc));  // row_bcast:31
+  return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 63));
 }
 __device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
-  return v;
+  const float id = 0.f;
+  v += TPR_DPP(v, id, 0xB1, 0xf);
+  v += TPR_DPP(v, id, 0x4E, 0xf);
+  v += TPR_DPP(v, id, 0x141, 0xf);
+  v += TPR_DPP(v, id, 0x140, 0xf);
+  v += TPR_DPP(v, id, 0x142, 0xa);
+  v += TPR_DPP(v, id, 0x143, 0xc);
+  return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 63));
 }
 
 __device__ __forceinline__ float lo16(uint32_t w) { return __uint_as_float(w << 16); }
@@ -63,6 +83,15 @@ __device__ __forceinline__ uint32_t pack_bf16(float a, float b) {
   const uint32_t x = __builtin_bit_cast(uint16_t, (__bf16)a);
   const uint32_t y = __builtin_bit_cast(uint16_t, (__bf16)b);
   return x | (y << 16);
+}
+__device__ __forceinline__ uint32_t pack_f16(float a, float b) {
+  const uint32_t x = __builtin_bit_cast(uint16_t, (_Float16)a);
+  const uint32_t y = __builtin_bit_cast(uint16_t, (_Float16)b);
+  return x | (y << 16);
+}
+__device__ __forceinline__ float f16_elem(const u32x4& v, int e) {
+  const uint32_t w = v[e >> 1];
+  return (float)__builtin_bit_cast(_Float16, (uint16_t)((e & 1) ? (w >> 16) : (w & 0xffffu)));
 }
 __device__ __forceinline__ float elem(const u32x4& v, int e) {
   const uint32_t w = v[e >> 1];
@@ -77,7 +106,6 @@ __global__ __launch_bounds__(CE_NT, 1) void ce_fast_kernel(const uint16_t* __res
   __shared__ float red_max[CE_NW][CE_PMAX];
   __shared__ float red_sum[CE_NW][CE_PMAX];
   __shared__ float sh_m[CE_PMAX], sh_s[CE_PMAX];
-  __shared__ float sh_t;
 
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
   const int64_t row = blockIdx.x;
@@ -89,7 +117,6 @@ __global__ __launch_bounds__(CE_NT, 1) void ce_fast_kernel(const uint16_t* __res
     (&red_max[0][0])[tid] = -INFINITY;
     (&red_sum[0][0])[tid] = 0.f;
   }
-  if (tid == 0) sh_t = 0.f;
 
   // Load the row once: slot s, lane tid owns vector vbeg[s] + tid.  Idle
   // lanes hold bf16 -inf, which drops out of the max and contributes exp = 0.
@@ -136,9 +163,10 @@ __global__ __launch_bounds__(CE_NT, 1) void ce_fast_kernel(const uint16_t* __res
   for (int r = 0; r < S.P; ++r) m = fmaxf(m, sh_m[r]);  // all-reduce(max)
   const float mL = m * LOG2E;
 
-  // Per-shard sums s_r with the global maximum, and the target term.
-  const int64_t vy = y >> 3;
-  const int ey = (int)(y & 7);
+  // Per-shard sums s_r with the global maximum.  The target logit is read once
+  // from memory (a uniform address); no per-element target test is needed.
+  const bool y_ok = y >= 0 && y < V;
+  const float zy = y_ok ? __uint_as_float((uint32_t)z[y_ok ? y : 0] << 16) : 0.f;
   {
     float run = 0.f;
     int cur = S.shard[0];
@@ -151,11 +179,14 @@ __global__ __launch_bounds__(CE_NT, 1) void ce_fast_kernel(const uint16_t* __res
         run = 0.f;
         cur = S.shard[s];
       }
-      float ls = 0.f;
+      // exp(z - m) once per logit: summed in fp32, then kept in place of the
+      // logit as fp16 (values in (0, 1]) for the gradient pass.
+      float ex[8];
 #pragma unroll
-      for (int e = 0; e < 8; ++e) ls += __builtin_amdgcn_exp2f(elem(v[s], e) * LOG2E - mL);
-      run += ls;
-      if ((int64_t)S.vbeg[s] + tid == vy && tid < S.nv[s]) sh_t = elem(v[s], ey) - m;
+      for (int e = 0; e < 8; ++e) ex[e] = __builtin_amdgcn_exp2f(elem(v[s], e) * LOG2E - mL);
+      run += ((ex[0] + ex[1]) + (ex[2] + ex[3])) + ((ex[4] + ex[5]) + (ex[6] + ex[7]));
+#pragma unroll
+      for (int q = 0; q < 4; ++q) v[s][q] = pack_f16(ex[2 * q], ex[2 * q + 1]);
     }
     if (S.nslot > 0) {
       const float w = wave_sum(run);
@@ -171,7 +202,7 @@ __global__ __launch_bounds__(CE_NT, 1) void ce_fast_kernel(const uint16_t* __res
   __syncthreads();
   float ssum = 0.f;
   for (int r = 0; r < S.P; ++r) ssum += sh_s[r];  // all-reduce(sum), rank order
-  const float t = sh_t;
+  const float t = y_ok ? zy - m : 0.f;  // the owning shard's target term
   if (tid == 0) row_loss[row] = logf(ssum) - t;
   if (stats != nullptr && tid < S.P) {
     const bool owns = y >= S.sbeg[tid] && y < S.sbeg[tid + 1];
@@ -181,23 +212,28 @@ __global__ __launch_bounds__(CE_NT, 1) void ce_fast_kernel(const uint16_t* __res
     st[2] = owns ? t : 0.f;
   }
 
-  // Gradient: (exp(z - m) / s - [j == y]) / T, rounded to bf16, written once.
+  // Gradient: exp(z - m) / s / T for every logit, rounded to bf16 and written
+  // once; the lane that wrote the vector holding the target then rewrites that
+  // element as (exp(z_y - m) / s - 1) / T (same thread, so program order makes
+  // the second store the final value).
   const float scale = invT / ssum;
+  const int vy = y_ok ? (int)(y >> 3) : -1;
+  bool owner = false;
 #pragma unroll
   for (int s = 0; s < CE_SLOTS; ++s) {
     if (s < S.nslot && tid < S.nv[s]) {
-      const int64_t vi = (int64_t)S.vbeg[s] + tid;
+      const int vi = S.vbeg[s] + tid;
+      owner |= vi == vy;
       float g[8];
 #pragma unroll
-      for (int e = 0; e < 8; ++e) g[e] = __builtin_amdgcn_exp2f(elem(v[s], e) * LOG2E - mL) * scale;
-      if (vi == vy) {
-#pragma unroll
-        for (int e = 0; e < 8; ++e)
-          if (e == ey) g[e] -= invT;
-      }
-      *reinterpret_cast<u32x4*>(dz + 8 * vi) =
+      for (int e = 0; e < 8; ++e) g[e] = f16_elem(v[s], e) * scale;
+      *reinterpret_cast<u32x4*>(dz + 8 * (int64_t)vi) =
           u32x4{pack_bf16(g[0], g[1]), pack_bf16(g[2], g[3]), pack_bf16(g[4], g[5]), pack_bf16(g[6], g[7])};
     }
+  }
+  if (owner) {
+    const float gy = __builtin_amdgcn_exp2f(zy * LOG2E - mL) * scale - invT;
+    dz[y] = __builtin_bit_cast(uint16_t, (__bf16)gy);
   }
 }
 
