@@ -15,6 +15,10 @@ are reported beside it.  Each call is timed with HIP events on the stream the
 library launches on.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline] [--copy-bytes N]
+       python bench.py --traffic-from FETCH_CSV WRITE_CSV COPY_BYTES
+The second form turns two rocprofv3 counter runs of the first form (one with
+--pmc FETCH_SIZE, one with --pmc WRITE_SIZE, both with --copy-bytes) into
+profiles/traffic.json; it needs no GPU.
 """
 import argparse
 import hashlib
@@ -59,35 +63,72 @@ def stored_traffic(kernel):
     return None if v is None else float(v)
 
 
-def cpu_baseline(budget_s=10.0):
-    """Time the fp64 oracle on a bounded sample of the MLP workload (a subset
-    of the tokens at the full 70B-rank d and f)."""
+GEMM_KERNEL = "gemm_bf16_dma_kernel"
+CE_KERNEL = "ce_fast_kernel"
+COPY_KERNEL = "neg_kernel"
+
+
+def traffic_from(fetch_csv, write_csv, copy_bytes):
+    """HBM bytes per launch from rocprofv3 counter_collection CSVs.
+
+    FETCH_SIZE / WRITE_SIZE are reported in KiB per dispatch; each is scaled
+    by copy_bytes / (what the same counter reads for the plain copy kernel of
+    copy_bytes read + copy_bytes written), so the figures are in true bytes.
+    """
+    import csv
+
+    def per_dispatch(path, counter):
+        rows = {}
+        with open(path) as f:
+            for r in csv.DictReader(f):
+                if r["Counter_Name"] == counter:
+                    key = int(r["Dispatch_Id"])
+                    rows[key] = (r["Kernel_Name"], rows.get(key, ("", 0.0))[1] + float(r["Counter_Value"]))
+        return [rows[k] for k in sorted(rows)]
+
+    out = {"kernel_source_digest": kernel_source_digest(), "copy_bytes": copy_bytes}
+    for counter, path in (("FETCH_SIZE", fetch_csv), ("WRITE_SIZE", write_csv)):
+        rows = per_dispatch(path, counter)
+        copy = [v for n, v in rows if COPY_KERNEL in n]
+        if len(copy) != 1:
+            raise SystemExit(f"{path}: expected one {COPY_KERNEL} dispatch, found {len(copy)}")
+        scale = copy_bytes / (copy[0] * 1024.0)
+        out[counter] = {"copy_kib": copy[0], "scale": scale}
+        for kernel in (GEMM_KERNEL, CE_KERNEL):
+            vals = [v * 1024.0 * scale for n, v in rows if kernel in n]
+            out[counter][kernel] = {"launches": len(vals), "avg_bytes": sum(vals) / max(len(vals), 1)}
+    for kernel in (GEMM_KERNEL, CE_KERNEL):
+        out[kernel + "_bytes_per_launch"] = (out["FETCH_SIZE"][kernel]["avg_bytes"] +
+                                             out["WRITE_SIZE"][kernel]["avg_bytes"])
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    with open(path, "w") as f:
+        json.dump(out, f, indent=1)
+        f.write("\n")
+    print(json.dumps(out, indent=1))
+
+
+def cpu_baseline(budget_s=10.0, max_reps=4):
+    """Time the fp64 oracle on the full 70B-rank MLP workload (all T tokens at
+    the same d and f), repeated until about budget_s seconds have passed."""
     import numpy as np
     import threadpoolctl
-    import torch
 
     import oracle
     import workloads
 
-    d, f = MLP["d"], MLP["f"]
-
-    def run(T):
-        x, w1, w2, gy = workloads.rank_mlp(T, d, f, seed=11, device="cpu")
-        xs = [t.float().numpy().astype(np.float64) for t in (x, w1, w2, gy)]
+    T, d, f = MLP["T"], MLP["d"], MLP["f"]
+    x, w1, w2, gy = workloads.rank_mlp(T, d, f, seed=11, device="cpu")
+    xs = [t.float().numpy().astype(np.float64) for t in (x, w1, w2, gy)]
+    times = []
+    while len(times) < max_reps and sum(times) < budget_s:
         t0 = time.perf_counter()
         oracle.mlp_fwd_bwd(*xs, "math")
-        return time.perf_counter() - t0
-
-    T = 64
-    dt = run(T)
-    T = int(min(MLP["T"], max(64, T * budget_s / max(dt, 1e-3))))
-    T -= T % 64
-    dt = run(T)
-    flops = 12.0 * T * d * f
+        times.append(time.perf_counter() - t0)
+    dt = sum(times) / len(times)
     threads = max([i.get("num_threads", 1) for i in threadpoolctl.threadpool_info()] + [1])
-    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
-            "sample": f"oracle.mlp_fwd_bwd (NumPy fp64) on T={T} of the 8192 tokens at d={d}, f={f}, "
-                      f"{dt:.2f} s, {os.cpu_count()} host CPUs visible"}
+    return {"value": 12.0 * T * d * f / dt / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+            "sample": f"oracle.mlp_fwd_bwd (NumPy fp64) on the full T={T}, d={d}, f={f} MLP, "
+                      f"{len(times)} runs of {dt:.2f} s on average, {os.cpu_count()} host CPUs visible"}
 
 
 def main():
@@ -96,10 +137,14 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--traffic-from", nargs=3, metavar=("FETCH_CSV", "WRITE_CSV", "COPY_BYTES"))
     ap.add_argument("--copy-bytes", type=int, default=0,
                     help="also run one plain copy kernel (torch.neg on fp32) of this many bytes before timing, "
                          "so that profiler byte counters can be calibrated against a known size")
     args = ap.parse_args()
+    if args.traffic_from:
+        traffic_from(args.traffic_from[0], args.traffic_from[1], int(args.traffic_from[2]))
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: every simulated tensor-parallel rank runs on that device. "
               "Runs on more than one GPU are not supported.", file=sys.stderr)
@@ -168,12 +213,16 @@ def main():
     inner_tflops = inner_flop / (avg(inner_ms) * 1e-3) / 1e12
     ce_gbs = ce_bytes / (avg(ce_ms) * 1e-3) / 1e9
 
-    # Dominant kernel: the bf16 MFMA GEMM (6 launches per MLP call, each
-    # 2*T*d*f FLOP; the tp=1 call launches nothing else).
-    gemm_launch_ms = avg(mlp_ms) / 6.0
-    gemm_achieved = (2.0 * T * d * f) / (gemm_launch_ms * 1e-3) / 1e12
-    gemm_traffic = stored_traffic("gemm_bf16_mlp_bytes_per_launch")
-    ce_traffic = stored_traffic("vocab_ce_bytes_per_launch")
+    # Dominant kernel: the bf16 MFMA GEMM.  Per step it is launched four times
+    # and nothing else runs in those two calls: the tp=1 MLP call makes three
+    # grouped launches ({fc1}, {fc2, dW2, dH}, {dW1, dx}) and the inner-axis
+    # call one ({Y, dA, dB}).  Average FLOP per launch / average launch time.
+    gemm_launches = 4
+    gemm_launch_ms = (avg(mlp_ms) + avg(inner_ms)) / gemm_launches
+    gemm_flop_per_launch = (mlp_flop + inner_flop) / gemm_launches
+    gemm_achieved = gemm_flop_per_launch / (gemm_launch_ms * 1e-3) / 1e12
+    gemm_traffic = stored_traffic(GEMM_KERNEL + "_bytes_per_launch")
+    ce_traffic = stored_traffic(CE_KERNEL + "_bytes_per_launch")
 
     line = {
         "metric": METRIC,
@@ -204,8 +253,10 @@ def main():
         "vocab_ce_pct_of_hbm_peak": round(100.0 * ce_gbs / PEAK_HBM_GBS, 2),
         "vocab_ce_ms": round(avg(ce_ms), 4),
         "roofline": {
-            "kernel": "gemm_bf16_kernel (MLP GEMMs, average of the 6 launches)",
+            "kernel": GEMM_KERNEL + " (4 grouped launches per step: 3 of the MLP call, 1 of the inner GEMM)",
             "bound": "mfma",
+            "flop_per_launch": gemm_flop_per_launch,
+            "avg_launch_us": round(gemm_launch_ms * 1e3, 2),
             "achieved": round(gemm_achieved, 2),
             "peak": PEAK_BF16_TFLOPS,
             "unit": "TFLOP/s",
@@ -213,8 +264,10 @@ def main():
             "traffic": gemm_traffic,
         },
         "roofline_ce": {
-            "kernel": "ce_fast_kernel + loss_mean_kernel (one call)",
+            "kernel": CE_KERNEL + " + loss_mean_kernel (one call)",
             "bound": "hbm",
+            "bytes_per_launch": ce_bytes,
+            "avg_call_us": round(avg(ce_ms) * 1e3, 2),
             "achieved": round(ce_gbs, 1),
             "peak": PEAK_HBM_GBS,
             "unit": "GB/s",
