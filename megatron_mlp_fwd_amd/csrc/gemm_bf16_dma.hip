@@ -2,25 +2,30 @@
 // every aligned bf16 product of the sharded GEMM page's 解题路线 and the TP
 // lesson's MLP; the register-staged kernel in gemm_bf16.hip covers the rest).
 //
-// Operand slabs go global -> LDS with buffer_load ... lds (16 bytes per lane,
-// no registers, out-of-range lanes read zeros through the buffer's range
-// check) into a 4-stage LDS ring of 32-deep k slabs (4 x 32 KB).  The 256 x
-// 256 block tile is computed by 8 waves (2 per SIMD) in a 2 x 4 grid, each
-// owning 128 x 64 outputs (8 x 4 MFMA 16x16 blocks).  Fragments
-// come out of LDS with ds_read_b128 for a k-major operand and with the gfx950
-// transpose read ds_read_b64_tr_b16 for an m/n-major one, so no layout needs a
-// transpose in registers.  Fragments are double-buffered in registers: the
-// reads for slab k+1 are issued between the two halves of slab k's 64 MFMAs,
-// after the one barrier per slab.
+// Block tile 256 x 256, 4 waves (one per SIMD) in a 2 x 2 grid, each owning a
+// 128 x 128 sub-tile = 8 x 8 blocks of v_mfma_f32_16x16x32_bf16 whose fp32
+// accumulators (256 per lane) stay pinned in AGPRs.  K advances in 64-deep
+// slabs through two 64 KB LDS stages.  Operands go global -> LDS with
+// buffer_load_dwordx4 ... lds (16 bytes per lane, no registers; the buffer's
+// range check zero-fills rows past the edge), so one wave instruction moves
+// 1 KB: 8 rows x 128 B of a k-major operand (whole cache lines) or 2 k-rows x
+// 512 B of an m/n-major one.  Fragments come out of LDS with ds_read_b128 for
+// a k-major operand and with the gfx950 transpose read ds_read_b64_tr_b16 for
+// an m/n-major one, so NN, NT and TN all run without register transposes.
 //
-// LDS layouts (16-byte chunks, XOR-swizzled so that every fragment read is
-// free of bank conflicts for 32- and 64-bank LDS phases):
-//   k-major tile:  16 blocks of 1 KB, block b = rows 16b..16b+15 x 4 chunks;
-//                  chunk c of row r sits at position 4 (r%16) + (c ^ kswz(r%16)).
-//   m/n-major tile: 32 k-rows of 512 B (256 elements); chunk c of k-row k sits
-//                  at 32 k + (c ^ mswz(k)).
-// The DMA of one wave instruction fills one 1 KB block lane-linearly, so each
-// lane fetches the global chunk that belongs at its LDS position.
+// Per slab k (stage k % 2): the first half (k 0..31) runs 64 MFMAs while the
+// second half's fragments are read; each wave then waits for its own DMA of
+// slab k+1, and one barrier makes slab k+1 visible and frees stage k % 2; the
+// second half runs 64 MFMAs with slab k+2's 16 DMA issues spread one per 4
+// MFMAs (a burst would stall the wave on a full address FIFO) and slab k+1's
+// first-half fragment reads one per 2 MFMAs.
+//
+// LDS layouts (16-byte chunks, XOR-swizzled so every fragment read is free of
+// bank conflicts under both a 16-lane/64-bank and an 8-lane/32-bank phase):
+//   k-major tile:  256 rows x 128 B; chunk c of row r sits at 8 r + (c ^ kswz(r)).
+//   m/n-major tile: 64 k-rows x 512 B; chunk c of k-row k sits at 32 k + (c ^ mswz(k)).
+#include <type_traits>
+
 #include "gemm_common.h"
 
 namespace tpr {
@@ -28,70 +33,117 @@ namespace {
 
 using namespace gemm;
 
-constexpr int BK = 32;                    // k per LDS stage
-constexpr int NS = 4;                     // LDS stages in flight
-constexpr int TILE_BYTES = 256 * BK * 2;  // one operand tile per stage: 16 KB
-constexpr int STAGE_BYTES = 2 * TILE_BYTES;
-constexpr int NT8 = 512;                  // 8 waves
-constexpr int TM8 = 128, TN8 = 64;        // wave tile
-constexpr int FM8 = TM8 / 16, FN8 = TN8 / 16;
-constexpr int LOADS_PER_STAGE = 4;        // DMA instructions per wave per stage (2 per operand)
-constexpr uint32_t OOB = 0x80000000u;     // voffset beyond every num_records: the load returns zeros
+constexpr int BK = 64;                       // k per LDS stage
+constexpr int TILE_BYTES = 256 * BK * 2;     // one operand tile per stage: 32 KB
+constexpr int STAGE_BYTES = 2 * TILE_BYTES;  // 64 KB; two stages
+constexpr int NTH = 256;                     // 4 waves, 2 x 2
+constexpr int WT = 128;                      // wave tile 128 x 128
+constexpr int FR = WT / 16;                  // fragments per operand per 32-deep half slab
+constexpr int NDMA = TILE_BYTES / 1024 / 4;  // DMA instructions per wave per operand per slab
+constexpr uint32_t OOB = 0x80000000u;        // voffset beyond every num_records: the load returns zeros
 
-static_assert(NS * STAGE_BYTES >= 8 * 32 * (TN8 + 4) * 4, "epilogue staging must fit in the stage ring");
+static_assert(2 * STAGE_BYTES >= 4 * 32 * (WT + 4) * 4, "epilogue staging must fit in the stage ring");
 
 typedef __attribute__((address_space(3))) uint8_t lds_u8;
-typedef short shortx4 __attribute__((ext_vector_type(4)));
-typedef __attribute__((address_space(3))) shortx4 lds_shortx4;
-typedef __attribute__((address_space(3))) bf16x8 lds_bf16x8;
 
-// A fragment is held as two 64-bit halves until it is consumed: the transpose
-// reads (inline assembly) write each half directly, and the halves are only
-// combined into the MFMA's 128-bit operand after the lgkmcnt wait that covers
-// them, so no register copy can ever read a half before its data has landed.
-struct Frag {
-  u32x2 lo, hi;
-};
-__device__ __forceinline__ bf16x8 as_operand(const Frag& f) {
-  return __builtin_bit_cast(bf16x8, u32x4{f.lo[0], f.lo[1], f.hi[0], f.hi[1]});
-}
-
-__device__ __forceinline__ int kswz(int rr) { return ((rr >> 1) & 3) ^ (((rr >> 3) & 1) * 3); }
+__device__ __forceinline__ int kswz(int r) { return (r & 7) ^ ((r >> 3) & 1); }
 __device__ __forceinline__ int mswz(int k) { return (2 * (k & 3)) ^ (8 * ((k >> 3) & 1)); }
+
+template <int I, int N, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+  if constexpr (I < N) {
+    f(std::integral_constant<int, I>{});
+    static_for<I + 1, N>(f);
+  }
+}
 
 // s_waitcnt with only a vmcnt limit (expcnt and lgkmcnt left at their maxima).
 template <int N>
 __device__ __forceinline__ void wait_vm() {
   __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
 }
-// Wait until at most n of this wave's loads are outstanding (n is uniform;
-// rounding it down to a supported count only waits longer).
-__device__ __forceinline__ void wait_vm_dyn(int n) {
-  if (n >= 8) wait_vm<8>();
-  else if (n >= 4) wait_vm<4>();
-  else wait_vm<0>();
+
+// Fragments are read with inline assembly (the builtin forms make the
+// compiler wait for every outstanding LDS DMA first, which would drain the
+// stage ring each slab).  A k-major fragment is one ds_read_b128; an m/n-major
+// one is two ds_read_b64_tr_b16 (k = 8G..8G+3 and 8G+4..8G+7 of the lane's
+// column), kept as two halves until the lgkmcnt wait that covers them, so no
+// register copy can read a half before its data has landed.
+struct FragK {
+  u32x4 v;
+};
+struct FragT {
+  u32x2 lo, hi;
+};
+__device__ __forceinline__ bf16x8 as_operand(const FragK& f) { return __builtin_bit_cast(bf16x8, f.v); }
+__device__ __forceinline__ bf16x8 as_operand(const FragT& f) {
+  return __builtin_bit_cast(bf16x8, u32x4{f.lo[0], f.lo[1], f.hi[0], f.hi[1]});
+}
+template <bool KMAJ>
+using Frag = typename std::conditional<KMAJ, FragK, FragT>::type;
+
+template <int OFF>
+__device__ __forceinline__ void read_frag(FragK& f, uint32_t addr) {
+  asm volatile("ds_read_b128 %0, %1 offset:%2" : "=v"(f.v) : "v"(addr), "i"(OFF));
+}
+template <int OFF>
+__device__ __forceinline__ void read_frag(FragT& f, uint32_t addr) {
+  asm volatile("ds_read_b64_tr_b16 %0, %2 offset:%3\n\tds_read_b64_tr_b16 %1, %2 offset:%4"
+               : "=&v"(f.lo), "=&v"(f.hi)
+               : "v"(addr), "i"(OFF), "i"(OFF + 2048));
 }
 
-struct DmaOperand {
+// Tie every fragment register to a point after an lgkmcnt wait.
+__device__ __forceinline__ void tie(FragK (&f)[FR]) {
+  asm volatile("" : "+v"(f[0].v), "+v"(f[1].v), "+v"(f[2].v), "+v"(f[3].v), "+v"(f[4].v), "+v"(f[5].v),
+               "+v"(f[6].v), "+v"(f[7].v));
+}
+__device__ __forceinline__ void tie(FragT (&f)[FR]) {
+  asm volatile("" : "+v"(f[0].lo), "+v"(f[0].hi), "+v"(f[1].lo), "+v"(f[1].hi), "+v"(f[2].lo), "+v"(f[2].hi),
+               "+v"(f[3].lo), "+v"(f[3].hi), "+v"(f[4].lo), "+v"(f[4].hi), "+v"(f[5].lo), "+v"(f[5].hi),
+               "+v"(f[6].lo), "+v"(f[6].hi), "+v"(f[7].lo), "+v"(f[7].hi));
+}
+template <bool AK, bool BKM>
+__device__ __forceinline__ void frag_wait(Frag<AK> (&a)[FR], Frag<BKM> (&b)[FR]) {
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+  tie(a);
+  tie(b);
+}
+
+// The accumulators live in AGPRs and are updated in place: inline assembly
+// pins each one to its registers (left to itself the compiler shuffles the
+// 256 accumulator registers between loop iterations).  The instruction reads
+// only its own AGPR accumulator, which nothing else writes, and VGPR operands
+// that LDS reads wrote behind an lgkmcnt wait; reading the accumulators after
+// the last MFMA is guarded by mfma_drain().
+__device__ __forceinline__ void mfma(floatx4& c, const bf16x8& a, const bf16x8& b) {
+  asm volatile("v_mfma_f32_16x16x32_bf16 %0, %1, %2, %0" : "+a"(c) : "v"(a), "v"(b));
+}
+__device__ __forceinline__ void mfma_drain() {
+  asm volatile("s_nop 15\n\ts_nop 15\n\ts_nop 15\n\ts_nop 15" ::: "memory");
+}
+
+struct Dma {
   __amdgpu_buffer_rsrc_t rsrc;
-  uint32_t voff[2];  // this lane's byte offsets for the wave's 2 loads of a stage (at k = 0)
-  uint32_t kstep;    // bytes between consecutive k slabs
+  uint32_t voff[NDMA];  // this lane's byte offsets for the wave's loads of one slab (at k = 0)
+  uint32_t kstep;       // bytes between consecutive k slabs
 };
 
 // Operand element (r, k): k-major at X[r * ld + k], m/n-major at X[k * ld + r].
+// Wave w fills 1 KB blocks NDMA w .. NDMA w + NDMA-1 of the 32 KB tile.
 template <bool KMAJ>
-__device__ __forceinline__ void dma_setup(DmaOperand& d, const void* X, int64_t ld, int R, int K, int r0, int wid,
+__device__ __forceinline__ void dma_setup(Dma& d, const void* X, int64_t ld, int R, int K, int r0, int wid,
                                           int lane) {
   const int64_t bytes = KMAJ ? ((int64_t)(R - 1) * ld + K) * 2 : ((int64_t)(K - 1) * ld + R) * 2;
   d.rsrc = __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(X), (short)0, (int)bytes, 0x00020000);
 #pragma unroll
-  for (int j = 0; j < 2; ++j) {
-    const int b = wid * 2 + j;
-    if constexpr (KMAJ) {
-      const int rr = lane >> 2, c = (lane & 3) ^ kswz(rr);
-      const int gr = r0 + 16 * b + rr;
+  for (int j = 0; j < NDMA; ++j) {
+    const int b = wid * NDMA + j;
+    if constexpr (KMAJ) {  // block b: rows 8b .. 8b+7, 8 chunks each
+      const int r = 8 * b + (lane >> 3), c = (lane & 7) ^ kswz(r);
+      const int gr = r0 + r;
       d.voff[j] = gr < R ? (uint32_t)(((int64_t)gr * ld + 8 * c) * 2) : OOB;
-    } else {
+    } else {  // block b: k-rows 2b, 2b+1, 32 chunks each
       const int kl = 2 * b + (lane >> 5), c = (lane & 31) ^ mswz(kl);
       const int gr = r0 + 8 * c;
       d.voff[j] = gr < R ? (uint32_t)(((int64_t)kl * ld + gr) * 2) : OOB;
@@ -100,217 +152,208 @@ __device__ __forceinline__ void dma_setup(DmaOperand& d, const void* X, int64_t 
   d.kstep = KMAJ ? BK * 2 : (uint32_t)(BK * ld * 2);
 }
 
-__device__ __forceinline__ void dma_issue(const DmaOperand& d, lds_u8* tile, int wid, int kt) {
-  lds_u8* base = tile + wid * 2 * 1024;
-  const uint32_t soff = (uint32_t)kt * d.kstep;
-#pragma unroll
-  for (int j = 0; j < 2; ++j)
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(d.rsrc, (__attribute__((address_space(3))) void*)(base + j * 1024), 16,
-                                             d.voff[j], soff, 0, 0);
-}
-
-__device__ __forceinline__ void dma_one(const DmaOperand& d, lds_u8* dst, int j, uint32_t soff) {
+__device__ __forceinline__ void dma_one(const Dma& d, lds_u8* dst, int j, uint32_t soff) {
   __builtin_amdgcn_raw_ptr_buffer_load_lds(d.rsrc, (__attribute__((address_space(3))) void*)dst, 16, d.voff[j], soff,
                                            0, 0);
 }
-
-// Per-lane LDS byte offsets of the NF fragments (rows row0 + 16 f .. +15) a
-// wave reads from one tile.
-template <bool KMAJ, int NF>
-__device__ __forceinline__ void frag_offsets(uint32_t (&off)[NF], int row0, int lane) {
+__device__ __forceinline__ void dma_all(const Dma& d, lds_u8* tile, int wid, int kt) {
+  lds_u8* base = tile + wid * NDMA * 1024;
+  const uint32_t soff = (uint32_t)kt * d.kstep;
 #pragma unroll
-  for (int f = 0; f < NF; ++f) {
-    if constexpr (KMAJ) {
-      const int rr = lane & 15, c = lane >> 4;
-      off[f] = (row0 / 16 + f) * 1024 + (rr * 4 + (c ^ kswz(rr))) * 16;
-    } else {
-      const int G = lane >> 4, q = lane & 15;
-      const int kl = 8 * G + (q >> 2);
+  for (int j = 0; j < NDMA; ++j) dma_one(d, base + j * 1024, j, soff);
+}
+// The last slab when K % 64 == 32: lanes whose k lies at or past K load
+// nothing (zeros), and the slab offset goes into the range-checked vector
+// offset, so no load can reach past the operand.
+template <bool KMAJ>
+__device__ __forceinline__ void dma_tail(const Dma& d, lds_u8* tile, int wid, int kt, int K, int lane) {
+  lds_u8* base = tile + wid * NDMA * 1024;
+  const uint32_t koff = (uint32_t)kt * d.kstep;
+#pragma unroll
+  for (int j = 0; j < NDMA; ++j) {
+    // k of this lane's chunk: k-major chunk index (lane & 7) ^ kswz(r) with
+    // r & 7 = lane >> 3 and (r >> 3) & 1 = j & 1; m/n-major k-row 2b + lane / 32.
+    const int kl = KMAJ ? 8 * ((lane & 7) ^ (lane >> 3) ^ (j & 1)) : 2 * (wid * NDMA + j) + (lane >> 5);
+    const uint32_t v = (kt * BK + kl < K && d.voff[j] != OOB) ? d.voff[j] + koff : OOB;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(d.rsrc, (__attribute__((address_space(3))) void*)(base + j * 1024), 16,
+                                             v, 0, 0, 0);
+  }
+}
+template <bool AK, bool BKM>
+__device__ __forceinline__ void dma_slab(const Dma& da, const Dma& db, lds_u8* stage, int wid, int kt, bool tail,
+                                         int K, int lane) {
+  if (tail) {
+    dma_tail<AK>(da, stage, wid, kt, K, lane);
+    dma_tail<BKM>(db, stage + TILE_BYTES, wid, kt, K, lane);
+  } else {
+    dma_all(da, stage, wid, kt);
+    dma_all(db, stage + TILE_BYTES, wid, kt);
+  }
+}
+
+// Per-lane LDS byte addresses of the fragments (rows row0 + 16 f ..) of one
+// operand; ds offsets are 16-bit immediates, so each stage has its own bases.
+// k-major: addr(s, f, h) = base[s][h] + 2048 f;  m/n-major: base[s][f] + 16384 h.
+template <bool KMAJ>
+struct FragAddr {
+  uint32_t base[2][KMAJ ? 2 : FR];
+};
+template <bool KMAJ>
+__device__ __forceinline__ void frag_addr(FragAddr<KMAJ>& fa, uint32_t tile0, int row0, int lane) {
+  if constexpr (KMAJ) {
+    const int rr = lane & 15, x = lane >> 4;
+#pragma unroll
+    for (int s = 0; s < 2; ++s)
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
+        fa.base[s][h] = tile0 + s * STAGE_BYTES + (row0 + rr) * 128 + (((4 * h + x) ^ kswz(rr)) * 16);
+  } else {
+    const int G = lane >> 4, q = lane & 15;
+    const int kl = 8 * G + (q >> 2);
+#pragma unroll
+    for (int f = 0; f < FR; ++f) {
       const int c = row0 / 8 + 2 * f + ((q & 3) >> 1);
-      off[f] = kl * 512 + ((c ^ mswz(kl)) * 16) + (q & 1) * 8;
+      fa.base[0][f] = tile0 + kl * 512 + ((c ^ mswz(kl)) * 16) + (q & 1) * 8;
+      fa.base[1][f] = fa.base[0][f] + STAGE_BYTES;
     }
   }
 }
-
-// Transpose read of one m/n-major fragment: two ds_read_b64_tr_b16 (k = 8G..8G+3
-// and 8G+4..8G+7 of the lane's row).  Issued as inline assembly because the
-// compiler places a wait for every outstanding LDS DMA in front of the builtin
-// form, which would drain the stage ring each slab; the caller therefore waits
-// on lgkmcnt itself (frag_wait) before the fragments are used.
-__device__ __forceinline__ Frag ds_read_tr_frag(uint32_t addr) {
-  Frag f;
-  asm volatile("ds_read_b64_tr_b16 %0, %2\n\tds_read_b64_tr_b16 %1, %2 offset:2048"
-               : "=&v"(f.lo), "=&v"(f.hi)
-               : "v"(addr));
-  return f;
-}
-
-template <bool KMAJ>
-__device__ __forceinline__ Frag read_frag(const lds_u8* tile, uint32_t off) {
-  if constexpr (KMAJ) {
-    const u32x4 v = *reinterpret_cast<const __attribute__((address_space(3))) u32x4*>(tile + off);
-    return Frag{u32x2{v[0], v[1]}, u32x2{v[2], v[3]}};
-  } else {
-    return ds_read_tr_frag((uint32_t)(uintptr_t)(tile + off));
-  }
-}
-
-template <bool KMAJ, int NF>
-__device__ __forceinline__ void read_frags(Frag (&fr)[NF], const lds_u8* tile, const uint32_t (&off)[NF]) {
-#pragma unroll
-  for (int f = 0; f < NF; ++f) fr[f] = read_frag<KMAJ>(tile, off[f]);
-}
-
-// Wait for this wave's outstanding LDS reads and make both halves of every
-// fragment depend on the wait, so nothing that reads them (MFMA operand
-// assembly included) can be scheduled above it.
-template <int NF>
-__device__ __forceinline__ void frag_wait(Frag (&fr)[NF]) {
-  static_assert(NF == 4 || NF == 8, "fragment count");
-  if constexpr (NF == 4) {
-    asm volatile("s_waitcnt lgkmcnt(0)"
-                 : "+v"(fr[0].lo), "+v"(fr[0].hi), "+v"(fr[1].lo), "+v"(fr[1].hi), "+v"(fr[2].lo), "+v"(fr[2].hi),
-                   "+v"(fr[3].lo), "+v"(fr[3].hi));
-  } else {
-    asm volatile("s_waitcnt lgkmcnt(0)"
-                 : "+v"(fr[0].lo), "+v"(fr[0].hi), "+v"(fr[1].lo), "+v"(fr[1].hi), "+v"(fr[2].lo), "+v"(fr[2].hi),
-                   "+v"(fr[3].lo), "+v"(fr[3].hi), "+v"(fr[4].lo), "+v"(fr[4].hi), "+v"(fr[5].lo), "+v"(fr[5].hi),
-                   "+v"(fr[6].lo), "+v"(fr[6].hi), "+v"(fr[7].lo), "+v"(fr[7].hi));
-  }
-}
-
-template <int NI0>
-__device__ __forceinline__ void mma_half(floatx4 (&acc)[FN8][FM8], const Frag (&a)[FM8], const Frag (&b)[FN8]) {
-#pragma unroll
-  for (int ni = NI0; ni < NI0 + FN8 / 2; ++ni)
-#pragma unroll
-    for (int mi = 0; mi < FM8; ++mi)
-      acc[ni][mi] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_operand(b[ni]), as_operand(a[mi]), acc[ni][mi], 0, 0, 0);
+// Read fragment F of half H from stage S.
+template <bool KMAJ, int S, int H, int F>
+__device__ __forceinline__ void read_one(Frag<KMAJ>& fr, const FragAddr<KMAJ>& fa) {
+  if constexpr (KMAJ) read_frag<F * 2048>(fr, fa.base[S][H]);
+  else read_frag<H * 16384>(fr, fa.base[S][F]);
 }
 
 // One 256 x 256 output tile of problem P.
 template <bool AK, bool BKM, int EPI>
 __device__ __forceinline__ void gemm_tile(const GemmProb& P, int tm, int tn, uint8_t* smem_raw, int vec_c) {
   lds_u8* smem = (lds_u8*)smem_raw;
-
+  const uint32_t lds0 = (uint32_t)(uintptr_t)smem;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int wm = wid >> 2, wn = wid & 3;
+  const int wm = wid >> 1, wn = wid & 1;
   const int M = P.M, N = P.N, K = P.K;
   const int m0 = tm * BM, n0 = tn * BN;
 
-  DmaOperand da, db;
+  Dma da, db;
   dma_setup<AK>(da, P.A, AK ? P.sa_m : P.sa_k, M, K, m0, wid, lane);
   dma_setup<BKM>(db, P.B, BKM ? P.sb_n : P.sb_k, N, K, n0, wid, lane);
-  uint32_t aoff[FM8], boff[FN8];
-  frag_offsets<AK, FM8>(aoff, wm * TM8, lane);
-  frag_offsets<BKM, FN8>(boff, wn * TN8, lane);
+  FragAddr<AK> aa;
+  FragAddr<BKM> ba;
+  frag_addr<AK>(aa, lds0, wm * WT, lane);
+  frag_addr<BKM>(ba, lds0 + TILE_BYTES, wn * WT, lane);
 
-  floatx4 acc[FN8][FM8];
+  floatx4 acc[FR][FR];
 #pragma unroll
-  for (int ni = 0; ni < FN8; ++ni)
+  for (int ni = 0; ni < FR; ++ni)
 #pragma unroll
-    for (int mi = 0; mi < FM8; ++mi) acc[ni][mi] = floatx4{0.f, 0.f, 0.f, 0.f};
+    for (int mi = 0; mi < FR; ++mi) acc[ni][mi] = floatx4{0.f, 0.f, 0.f, 0.f};
 
-  const int nk = K / BK;
+  const int nk = (K + BK - 1) / BK;  // 64-deep slabs; the last one is half used when K % 64 == 32
+  const bool half_tail = (K % BK) != 0;
+  Frag<AK> a0[FR], a1[FR];
+  Frag<BKM> b0[FR], b1[FR];
+  using I0 = std::integral_constant<int, 0>;
+  using I1 = std::integral_constant<int, 1>;
+
+  // All fragments of half H of stage S into (a, b), in program order.
+  auto read_half = [&](auto S_, auto H_, Frag<AK>(&a)[FR], Frag<BKM>(&b)[FR]) {
+    constexpr int S = decltype(S_)::value, H = decltype(H_)::value;
+    static_for<0, FR>([&](auto f_) {
+      constexpr int f = decltype(f_)::value;
+      read_one<AK, S, H, f>(a[f], aa);
+    });
+    static_for<0, FR>([&](auto f_) {
+      constexpr int f = decltype(f_)::value;
+      read_one<BKM, S, H, f>(b[f], ba);
+    });
+  };
+  // The 64 MFMAs of one half slab (acc[ni][mi] += B fragment ni x A fragment mi).
+  auto mma_half = [&](const Frag<AK>(&a)[FR], const Frag<BKM>(&b)[FR]) {
+#pragma unroll
+    for (int ni = 0; ni < FR; ++ni)
+#pragma unroll
+      for (int mi = 0; mi < FR; ++mi) mfma(acc[ni][mi], as_operand(b[ni]), as_operand(a[mi]));
+  };
+
   if (nk > 0) {
-    // Prologue: stages 0 .. NS-2 in flight, wait for stage 0, read its fragments.
-#pragma unroll
-    for (int s = 0; s < NS - 1; ++s)
-      if (s < nk) {
-        dma_issue(da, smem + s * STAGE_BYTES, wid, s);
-        dma_issue(db, smem + s * STAGE_BYTES + TILE_BYTES, wid, s);
-      }
-    wait_vm_dyn(min(NS - 2, nk - 1) * LOADS_PER_STAGE);
-    __builtin_amdgcn_s_barrier();
-
-    Frag fa[2][FM8], fb[2][FN8];
-    read_frags<AK, FM8>(fa[0], smem, aoff);
-    read_frags<BKM, FN8>(fb[0], smem + TILE_BYTES, boff);
-
-    // One slab per step; the fragment register sets alternate, so loops cover
-    // a pair of slabs.  `step` is the general form (any position, guarded);
-    // `steady` is the branch-free form used while every slab still has a
-    // successor to read and a slab to prefetch.  In `steady` the second half
-    // of the MFMAs is interleaved with the slab's 4 DMA issues and the next
-    // fragment reads, and scheduling fences keep the first half ahead of the
-    // barrier (the MFMAs carry no memory dependency the compiler could see).
-    auto step = [&](int kt, Frag(&ca)[FM8], Frag(&cb)[FN8], Frag(&na)[FM8], Frag(&nb)[FN8]) {
-      frag_wait<FM8>(ca);
-      frag_wait<FN8>(cb);
-      mma_half<0>(acc, ca, cb);
-      if (kt + 1 < nk) {
-        wait_vm_dyn((min(kt + NS - 2, nk - 1) - (kt + 1)) * LOADS_PER_STAGE);
-        __builtin_amdgcn_s_barrier();
-        const int s_new = kt + NS - 1;
-        if (s_new < nk) {
-          lds_u8* st = smem + (s_new % NS) * STAGE_BYTES;
-          dma_issue(da, st, wid, s_new);
-          dma_issue(db, st + TILE_BYTES, wid, s_new);
-        }
-        const lds_u8* nx = smem + ((kt + 1) % NS) * STAGE_BYTES;
-        read_frags<AK, FM8>(na, nx, aoff);
-        read_frags<BKM, FN8>(nb, nx + TILE_BYTES, boff);
-      }
-      mma_half<FN8 / 2>(acc, ca, cb);
-    };
-    auto steady = [&](int kt, Frag(&ca)[FM8], Frag(&cb)[FN8], Frag(&na)[FM8], Frag(&nb)[FN8]) {
-      frag_wait<FM8>(ca);
-      frag_wait<FN8>(cb);
-      mma_half<0>(acc, ca, cb);
-      __builtin_amdgcn_sched_barrier(0);
-      wait_vm<(NS - 3) * LOADS_PER_STAGE>();
-      __builtin_amdgcn_s_barrier();
-      __builtin_amdgcn_sched_barrier(0);
-      const int s_new = kt + NS - 1;
-      lds_u8* st = smem + (s_new % NS) * STAGE_BYTES;
-      const lds_u8* nx = smem + ((kt + 1) % NS) * STAGE_BYTES;
-      const uint32_t soa = (uint32_t)s_new * da.kstep, sob = (uint32_t)s_new * db.kstep;
-      lds_u8* dsta = st + wid * 2 * 1024;
-      lds_u8* dstb = st + TILE_BYTES + wid * 2 * 1024;
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const int ni = FN8 / 2 + i / FM8, mi = i % FM8;
-        acc[ni][mi] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_operand(cb[ni]), as_operand(ca[mi]), acc[ni][mi], 0, 0, 0);
-        if (i == 0) dma_one(da, dsta, 0, soa);
-        if (i == 2) dma_one(da, dsta + 1024, 1, soa);
-        if (i == 4) dma_one(db, dstb, 0, sob);
-        if (i == 6) dma_one(db, dstb + 1024, 1, sob);
-        if (i >= 1 && i < 1 + FM8) na[i - 1] = read_frag<AK>(nx, aoff[i - 1]);
-        if (i >= 1 + FM8 && i < 1 + FM8 + FN8) nb[i - 1 - FM8] = read_frag<BKM>(nx + TILE_BYTES, boff[i - 1 - FM8]);
-      }
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
-        __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);  // one VMEM (the DMA)
-      }
-#pragma unroll
-      for (int i = 0; i < 12; ++i) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
-        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // one LDS read
-      }
-      __builtin_amdgcn_sched_barrier(0);
-    };
-    int kt = 0;
-    for (; kt + NS < nk; kt += 2) {
-      steady(kt, fa[0], fb[0], fa[1], fb[1]);
-      steady(kt + 1, fa[1], fb[1], fa[0], fb[0]);
+    // Prologue: slabs 0 and 1 in flight, wait for slab 0, read its first half.
+    dma_slab<AK, BKM>(da, db, smem, wid, 0, half_tail && nk == 1, K, lane);
+    if (nk > 1) {
+      dma_slab<AK, BKM>(da, db, smem + STAGE_BYTES, wid, 1, half_tail && nk == 2, K, lane);
+      wait_vm<2 * NDMA>();
+    } else {
+      wait_vm<0>();
     }
-    for (; kt < nk; kt += 2) {
-      step(kt, fa[0], fb[0], fa[1], fb[1]);
-      if (kt + 1 < nk) step(kt + 1, fa[1], fb[1], fa[0], fb[0]);
+    __builtin_amdgcn_s_barrier();
+    read_half(I0{}, I0{}, a0, b0);
+
+    // General form of slab k (stage S = k % 2): any position, guarded.
+    auto slab = [&](auto S_, int k) {
+      constexpr int S = decltype(S_)::value;
+      const bool full = !(half_tail && k == nk - 1);
+      frag_wait<AK, BKM>(a0, b0);
+      if (full) read_half(S_, I1{}, a1, b1);
+      mma_half(a0, b0);
+      if (k + 1 < nk) wait_vm<0>();
+      frag_wait<AK, BKM>(a1, b1);
+      if (k + 1 < nk) {
+        __builtin_amdgcn_s_barrier();
+        if (k + 2 < nk)
+          dma_slab<AK, BKM>(da, db, smem + S * STAGE_BYTES, wid, k + 2, half_tail && k + 2 == nk - 1, K, lane);
+        read_half(std::integral_constant<int, 1 - S>{}, I0{}, a0, b0);
+      }
+      if (full) mma_half(a1, b1);
+    };
+    // Branch-free form for slabs whose successor exists and whose k+2
+    // prefetch is a full slab, with the memory instructions interleaved.
+    auto steady = [&](auto S_, int k) {
+      constexpr int S = decltype(S_)::value;
+      frag_wait<AK, BKM>(a0, b0);
+      static_for<0, 64>([&](auto i_) {
+        constexpr int i = decltype(i_)::value, r = i / 2;
+        mfma(acc[i / FR][i % FR], as_operand(b0[i / FR]), as_operand(a0[i % FR]));
+        if constexpr ((i & 1) && r < FR) read_one<AK, S, 1, r>(a1[r], aa);
+        if constexpr ((i & 1) && r >= FR && r < 2 * FR) read_one<BKM, S, 1, r - FR>(b1[r - FR], ba);
+      });
+      wait_vm<0>();
+      frag_wait<AK, BKM>(a1, b1);
+      __builtin_amdgcn_s_barrier();
+      const uint32_t soa = (uint32_t)(k + 2) * da.kstep, sob = (uint32_t)(k + 2) * db.kstep;
+      lds_u8* dsta = smem + S * STAGE_BYTES + wid * NDMA * 1024;
+      lds_u8* dstb = dsta + TILE_BYTES;
+      static_for<0, 64>([&](auto i_) {
+        constexpr int i = decltype(i_)::value, j = i / 4, r = (i - 1) / 2;
+        mfma(acc[i / FR][i % FR], as_operand(b1[i / FR]), as_operand(a1[i % FR]));
+        if constexpr (i % 4 == 0 && j < NDMA) dma_one(da, dsta + j * 1024, j, soa);
+        if constexpr (i % 4 == 0 && j >= NDMA) dma_one(db, dstb + (j - NDMA) * 1024, j - NDMA, sob);
+        if constexpr ((i & 1) && r < FR) read_one<AK, 1 - S, 0, r>(a0[r], aa);
+        if constexpr ((i & 1) && r >= FR && r < 2 * FR) read_one<BKM, 1 - S, 0, r - FR>(b0[r - FR], ba);
+      });
+    };
+    const int lim = half_tail ? nk - 1 : nk;  // slabs below lim are full
+    int k = 0;
+    for (; k + 3 < lim; k += 2) {
+      steady(I0{}, k);
+      steady(I1{}, k + 1);
+    }
+    for (; k < nk; k += 2) {
+      slab(I0{}, k);
+      if (k + 1 < nk) slab(I1{}, k + 1);
     }
   }
+  mfma_drain();
   __syncthreads();
-  epilogue_via_lds<EPI, TM8, TN8>(reinterpret_cast<float*>(smem_raw), acc, P, m0, n0, wid, wm, wn, lane, vec_c);
+  epilogue_via_lds<EPI, WT, WT>(reinterpret_cast<float*>(smem_raw), acc, P, m0, n0, wid, wm, wn, lane, vec_c);
 }
 
 // Block -> (problem, tile).  Every problem's tiles start at a multiple of 8
 // blocks (padding blocks exit), so a block's XCD (blockIdx % 8, the hardware's
 // round-robin) is its position within the problem modulo 8; each XCD gets one
 // contiguous run of the problem's tiles, walked in grouped raster order.
-__global__ __launch_bounds__(NT8, 1) void gemm_bf16_dma_kernel(const GemmBatch batch) {
-  __shared__ __attribute__((aligned(1024))) uint8_t smem_raw[NS * STAGE_BYTES];
+__global__ __launch_bounds__(NTH, 1) void gemm_bf16_dma_kernel(const GemmBatch batch) {
+  __shared__ __attribute__((aligned(1024))) uint8_t smem_raw[2 * STAGE_BYTES];
   const int bid = blockIdx.x;
   int g = 0;
 #pragma unroll
@@ -345,13 +388,14 @@ bool aligned(const void* p, int bytes) { return (reinterpret_cast<uintptr_t>(p) 
 
 }  // namespace
 
-// Eligibility of a problem for the direct-to-LDS kernel: K a multiple of the
-// 32-deep slab, 16-byte aligned rows along each operand's contiguous
-// dimension, an extent along it that is a multiple of 8 elements, operand byte
-// ranges that the 32-bit buffer offsets can address, and a (layout, epilogue)
-// pair the kernel instantiates (the GELU epilogues need a k-major A).
+// Eligibility of a problem for the direct-to-LDS kernel: K a multiple of 32
+// (whole MFMA steps; a last half slab is handled), 16-byte aligned rows along
+// each operand's contiguous dimension, an extent along it that is a multiple
+// of 8 elements, operand byte ranges that the 32-bit buffer offsets can
+// address, and a (layout, epilogue) pair the kernel instantiates (the GELU
+// epilogues need a k-major A).
 bool gemm_bf16_dma_eligible(const GemmProb& p, bool a_kmajor, bool b_kmajor, int epi) {
-  if (p.M <= 0 || p.N <= 0 || p.K <= 0 || p.K % BK != 0) return false;
+  if (p.M <= 0 || p.N <= 0 || p.K <= 0 || p.K % 32 != 0) return false;
   if (epi != EPI_F32 && !a_kmajor) return false;
   const int64_t a_ld = a_kmajor ? p.sa_m : p.sa_k, b_ld = b_kmajor ? p.sb_n : p.sb_k;
   if ((a_kmajor ? p.sa_k : p.sa_m) != 1 || (b_kmajor ? p.sb_k : p.sb_n) != 1) return false;
@@ -382,7 +426,7 @@ hipError_t launch_gemm_bf16_dma(GemmBatch& b, hipStream_t s) {
   }
   b.total_tiles = total;
   if (total == 0) return hipSuccess;
-  hipLaunchKernelGGL(gemm_bf16_dma_kernel, dim3(total), dim3(NT8), 0, s, b);
+  hipLaunchKernelGGL(gemm_bf16_dma_kernel, dim3(total), dim3(NTH), 0, s, b);
   return hipGetLastError();
 }
 
