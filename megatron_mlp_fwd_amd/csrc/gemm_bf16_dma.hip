@@ -49,14 +49,6 @@ typedef __attribute__((address_space(3))) uint8_t lds_u8;
 __device__ __forceinline__ int kswz(int r) { return (r & 7) ^ ((r >> 3) & 1); }
 __device__ __forceinline__ int mswz(int k) { return (2 * (k & 3)) ^ (8 * ((k >> 3) & 1)); }
 
-template <int I, int N, typename F>
-__device__ __forceinline__ void static_for(F&& f) {
-  if constexpr (I < N) {
-    f(std::integral_constant<int, I>{});
-    static_for<I + 1, N>(f);
-  }
-}
-
 // s_waitcnt with only a vmcnt limit (expcnt and lgkmcnt left at their maxima).
 template <int N>
 __device__ __forceinline__ void wait_vm() {
@@ -359,7 +351,7 @@ __global__ __launch_bounds__(NTH, 1) void gemm_bf16_dma_kernel(const GemmBatch b
 #pragma unroll
   for (int i = 1; i < kMaxGroup; ++i)
     if (i < batch.count && bid >= batch.p[i].tile_start) g = i;
-  const GemmProb& P = batch.p[g];
+  const GemmProb P = batch.p[g];  // a copy: keeps the by-value batch out of scratch
   const int ntiles = P.tiles_m * P.tiles_n;
   const int l = bid - P.tile_start;
   const int per_xcd = (ntiles + 7) >> 3;

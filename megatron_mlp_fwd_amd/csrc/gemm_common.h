@@ -3,6 +3,8 @@
 // the epilogue (staged through LDS so that stores are row-contiguous).
 #pragma once
 
+#include <type_traits>
+
 #include "common.h"
 
 namespace tpr {
@@ -21,6 +23,15 @@ constexpr int WTM = 128, WTN = 128;
 constexpr int FM = WTM / 16, FN = WTN / 16;
 constexpr int GROUP_M = 8;  // tile rows per raster group (L2 reuse of the B panel)
 
+// Compile-time loop: f(std::integral_constant<int, I>) for I = I0 .. N-1.
+template <int I, int N, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+  if constexpr (I < N) {
+    f(std::integral_constant<int, I>{});
+    static_for<I + 1, N>(f);
+  }
+}
+
 __device__ __forceinline__ uint32_t pack_bf16(float a, float b) {
   const uint32_t x = __builtin_bit_cast(uint16_t, (__bf16)a);
   const uint32_t y = __builtin_bit_cast(uint16_t, (__bf16)b);
@@ -29,10 +40,33 @@ __device__ __forceinline__ uint32_t pack_bf16(float a, float b) {
 __device__ __forceinline__ float bf_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
 
-// Exact-erf GELU and its derivative (fp32).  Phi(x) = erfc(-x/sqrt2)/2.
-__device__ __forceinline__ float gelu_f(float x) { return 0.5f * x * erfcf(-0.70710678118654752f * x); }
+// The exact-erf GELU x Phi(x) and its derivative Phi(x) + x phi(x) for the
+// bf16 kernels, whose pre-activation and results are rounded to bf16.  Phi
+// comes from the Abramowitz-Stegun 7.1.26 (Hastings) form of erfc,
+// erfc(z) = (a1 t + ... + a5 t^5) exp(-z^2), t = 1 / (1 + p z), z >= 0, whose
+// error is below 1.5e-7; evaluated in fp32 the error in Phi, gelu and gelu'
+// stays below 5e-7 absolute (and below 6e-5 relative for gelu at
+// 0.01 < |x| < 3), far under bf16's 2^-8.  exp(-x^2/2) is shared by erfc and
+// phi.  Costs about 15 VALU operations instead of a full-precision erfcf.
+struct PhiExp {
+  float Phi;  // Phi(x)
+  float e;    // exp(-x^2 / 2)
+};
+__device__ __forceinline__ PhiExp phi_exp(float x) {
+  const float z = fabsf(x) * 0.70710678118654752f;
+  const float t = __builtin_amdgcn_rcpf(fmaf(0.3275911f, z, 1.0f));
+  float p = fmaf(t, 1.061405429f, -1.453152027f);
+  p = fmaf(t, p, 1.421413741f);
+  p = fmaf(t, p, -0.284496736f);
+  p = fmaf(t, p, 0.254829592f);
+  const float e = __builtin_amdgcn_exp2f(-0.72134752044448170f * x * x);  // 1 / (2 ln 2)
+  const float q = 0.5f * p * t * e;  // Phi(-|x|)
+  return PhiExp{x >= 0.f ? 1.f - q : q, e};
+}
+__device__ __forceinline__ float gelu_f(float x) { return x * phi_exp(x).Phi; }
 __device__ __forceinline__ float gelu_prime_f(float x) {
-  return 0.5f * erfcf(-0.70710678118654752f * x) + 0.39894228040143268f * x * expf(-0.5f * x * x);
+  const PhiExp r = phi_exp(x);
+  return fmaf(0.39894228040143268f * x, r.e, r.Phi);
 }
 
 // Workgroups are handed to the 8 XCDs round-robin; renumber so that each XCD
@@ -63,8 +97,11 @@ __device__ __forceinline__ TileCoord locate_tile(const GemmBatch& batch) {
 }
 
 // Apply the epilogue to four consecutive outputs C[m][n .. n+3] (off = m*ldc+n).
+// For EPI_DGELU, `pre` holds the four bf16 pre-activations when the caller
+// prefetched them (full vector rows); otherwise they are loaded here.
 template <int EPI>
-__device__ __forceinline__ void epilogue_store(const GemmProb& P, floatx4 v, int64_t off, int n, int N, int vec_c) {
+__device__ __forceinline__ void epilogue_store(const GemmProb& P, floatx4 v, int64_t off, int n, int N, int vec_c,
+                                               u32x2 pre = u32x2{0u, 0u}) {
   const bool full = vec_c && (n + 3 < N);
   if constexpr (EPI == EPI_F32) {
     float* c = static_cast<float*>(P.C) + off;
@@ -90,20 +127,19 @@ __device__ __forceinline__ void epilogue_store(const GemmProb& P, floatx4 v, int
         }
     }
   } else {  // EPI_DGELU: C = acc * gelu'(pre), pre read from aux_in (may alias C)
-    const uint16_t* p = static_cast<const uint16_t*>(P.aux_in) + off;
     uint16_t* c = static_cast<uint16_t*>(P.C) + off;
     if (full) {
-      const u32x2 pw = *reinterpret_cast<const u32x2*>(p);
-      v[0] *= gelu_prime_f(bf_lo(pw[0]));
-      v[1] *= gelu_prime_f(bf_hi(pw[0]));
-      v[2] *= gelu_prime_f(bf_lo(pw[1]));
-      v[3] *= gelu_prime_f(bf_hi(pw[1]));
+      v[0] *= gelu_prime_f(bf_lo(pre[0]));
+      v[1] *= gelu_prime_f(bf_hi(pre[0]));
+      v[2] *= gelu_prime_f(bf_lo(pre[1]));
+      v[3] *= gelu_prime_f(bf_hi(pre[1]));
       *reinterpret_cast<u32x2*>(c) = u32x2{pack_bf16(v[0], v[1]), pack_bf16(v[2], v[3])};
     } else {
+      const uint16_t* p = static_cast<const uint16_t*>(P.aux_in) + off;
       for (int r = 0; r < 4; ++r)
         if (n + r < N) {
-          const float pre = __uint_as_float((uint32_t)p[r] << 16);
-          c[r] = __builtin_bit_cast(uint16_t, (__bf16)(v[r] * gelu_prime_f(pre)));
+          const float x = __uint_as_float((uint32_t)p[r] << 16);
+          c[r] = __builtin_bit_cast(uint16_t, (__bf16)(v[r] * gelu_prime_f(x)));
         }
     }
   }
@@ -112,9 +148,11 @@ __device__ __forceinline__ void epilogue_store(const GemmProb& P, floatx4 v, int
 // Epilogue through LDS (`stage` must be free and hold 32 * (TN_ + 4) floats per
 // wave).  Pass q moves MFMA blocks mi = 2q, 2q+1 of every wave (a 32 x TN_
 // region per wave) into LDS, then each wave reads its region back
-// row-contiguously and applies the epilogue with coalesced stores.  The wave
-// (wm, wn) owns rows wm*TM_ .. and columns wn*TN_ .. of the block tile, and
-// acc[ni][mi] holds C[m0 + wm*TM_ + mi*16 + lane%16][n0 + wn*TN_ + ni*16 + 4*(lane/16) + r].
+// row-contiguously and applies the epilogue with coalesced stores.  For
+// EPI_DGELU the pass's pre-activations are loaded before the LDS exchange so
+// their latency overlaps it.  The wave (wm, wn) owns rows wm*TM_ .. and
+// columns wn*TN_ .. of the block tile, and acc[ni][mi] holds
+// C[m0 + wm*TM_ + mi*16 + lane%16][n0 + wn*TN_ + ni*16 + 4*(lane/16) + r].
 template <int EPI, int TM_, int TN_>
 __device__ __forceinline__ void epilogue_via_lds(float* stage, const floatx4 (&acc)[TN_ / 16][TM_ / 16],
                                                  const GemmProb& P, int m0, int n0, int wid, int wm, int wn,
@@ -122,11 +160,28 @@ __device__ __forceinline__ void epilogue_via_lds(float* stage, const floatx4 (&a
   constexpr int LD = TN_ + 4;
   constexpr int LANES_PER_ROW = TN_ / 4;
   constexpr int ROWS_PER_IT = 64 / LANES_PER_ROW;
+  constexpr int ITS = 32 / ROWS_PER_IT;
   float* ep = stage + wid * (32 * LD);
   const int64_t ldc = P.ldc;
   const int M = P.M, N = P.N;
+  const int col = 4 * (lane % LANES_PER_ROW);
+  const int n = n0 + wn * TN_ + col;
+  const bool vec_n = vec_c && n + 3 < N;
+  // Passes are unrolled at compile time (static_for), so acc is only ever
+  // indexed by constants and stays in registers.
+  static_for<0, TM_ / 32>([&](auto q_) {
+    constexpr int q = decltype(q_)::value;
+    const int mbase = m0 + wm * TM_ + 32 * q + lane / LANES_PER_ROW;
+    u32x2 pre[ITS];
+    if constexpr (EPI == EPI_DGELU) {
 #pragma unroll
-  for (int q = 0; q < TM_ / 32; ++q) {
+      for (int it = 0; it < ITS; ++it) {
+        const int m = mbase + ROWS_PER_IT * it;
+        pre[it] = (vec_n && m < M)
+                      ? *reinterpret_cast<const u32x2*>(static_cast<const uint16_t*>(P.aux_in) + (int64_t)m * ldc + n)
+                      : u32x2{0u, 0u};
+      }
+    }
 #pragma unroll
     for (int h = 0; h < 2; ++h)
 #pragma unroll
@@ -134,18 +189,20 @@ __device__ __forceinline__ void epilogue_via_lds(float* stage, const floatx4 (&a
         *reinterpret_cast<floatx4*>(ep + (h * 16 + (lane & 15)) * LD + ni * 16 + 4 * (lane >> 4)) =
             acc[ni][2 * q + h];
     __syncthreads();
-    const int col = 4 * (lane % LANES_PER_ROW);
-    const int n = n0 + wn * TN_ + col;
-    for (int it = 0; it < 32 / ROWS_PER_IT; ++it) {
+#pragma unroll
+    for (int it = 0; it < ITS; ++it) {
       const int row = ROWS_PER_IT * it + lane / LANES_PER_ROW;
-      const int m = m0 + wm * TM_ + 32 * q + row;
+      const int m = mbase + ROWS_PER_IT * it;
       if (m < M && n < N) {
-        floatx4 v = *reinterpret_cast<const floatx4*>(ep + row * LD + col);
-        epilogue_store<EPI>(P, v, (int64_t)m * ldc + n, n, N, vec_c);
+        const floatx4 v = *reinterpret_cast<const floatx4*>(ep + row * LD + col);
+        if constexpr (EPI == EPI_DGELU)
+          epilogue_store<EPI>(P, v, (int64_t)m * ldc + n, n, N, vec_c, pre[it]);
+        else
+          epilogue_store<EPI>(P, v, (int64_t)m * ldc + n, n, N, vec_c);
       }
     }
     __syncthreads();
-  }
+  });
 }
 
 }  // namespace gemm
