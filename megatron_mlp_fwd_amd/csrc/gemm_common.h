@@ -104,12 +104,15 @@ __device__ __forceinline__ void epilogue_store(const GemmProb& P, floatx4 v, int
                                                u32x2 pre = u32x2{0u, 0u}) {
   const bool full = vec_c && (n + 3 < N);
   if constexpr (EPI == EPI_F32) {
+    // fp32 results are final outputs, not read again by the kernels of the
+    // same call: non-temporal stores keep them from displacing the operand
+    // panels that the running tiles share in L2.
     float* c = static_cast<float*>(P.C) + off;
     if (full) {
-      *reinterpret_cast<floatx4*>(c) = v;
+      __builtin_nontemporal_store(v, reinterpret_cast<floatx4*>(c));
     } else {
       for (int r = 0; r < 4; ++r)
-        if (n + r < N) c[r] = v[r];
+        if (n + r < N) __builtin_nontemporal_store(v[r], c + r);
     }
   } else if constexpr (EPI == EPI_GELU) {
     uint16_t* c = static_cast<uint16_t*>(P.C) + off;
