@@ -93,11 +93,18 @@ __device__ __forceinline__ float f16_elem(const u32x4& v, int e) {
   const uint32_t w = v[e >> 1];
   return (float)__builtin_bit_cast(_Float16, (uint16_t)((e & 1) ? (w >> 16) : (w & 0xffffu)));
 }
+// Maximum of the 8 bf16 logits of a vector.
+__device__ __forceinline__ float vec_max(const u32x4& v) {
+  const float a = fmaxf(fmaxf(lo16(v[0]), hi16(v[0])), lo16(v[1]));
+  const float b = fmaxf(fmaxf(hi16(v[1]), lo16(v[2])), hi16(v[2]));
+  return fmaxf(fmaxf(a, b), fmaxf(lo16(v[3]), hi16(v[3])));
+}
 __device__ __forceinline__ float elem(const u32x4& v, int e) {
   const uint32_t w = v[e >> 1];
   return (e & 1) ? hi16(w) : lo16(w);
 }
 
+template <bool STATS>
 __global__ __launch_bounds__(CE_NT, 1) void ce_fast_kernel(const uint16_t* __restrict__ logits,
                                                           const int64_t* __restrict__ labels,
                                                           uint16_t* __restrict__ dlogits, float* __restrict__ row_loss,
@@ -124,14 +131,16 @@ __global__ __launch_bounds__(CE_NT, 1) void ce_fast_kernel(const uint16_t* __res
 #pragma unroll
   for (int s = 0; s < CE_SLOTS; ++s) {
     const bool on = s < S.nslot && tid < S.nv[s];
-    v[s] = on ? *reinterpret_cast<const u32x4*>(z + 8 * ((int64_t)S.vbeg[s] + tid))
+    v[s] = on ? __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(z + 8 * ((int64_t)S.vbeg[s] + tid)))
               : u32x4{0xff80ff80u, 0xff80ff80u, 0xff80ff80u, 0xff80ff80u};
   }
   __syncthreads();
 
-  // Per-shard maxima m_r: running max over the slots of one shard, flushed
-  // (wave reduce, one LDS word per wave) when the slot's shard changes.
-  {
+  // Maxima.  With per-shard statistics requested: m_r per shard, a running
+  // max over the slots of one shard flushed (wave reduce, one LDS word per
+  // wave) when the slot's shard changes, then m = max_r m_r.  Otherwise only
+  // the row maximum m is formed (the same value; one wave reduce per wave).
+  if constexpr (STATS) {
     float run = -INFINITY;
     int cur = S.shard[0];
 #pragma unroll
@@ -143,24 +152,34 @@ __global__ __launch_bounds__(CE_NT, 1) void ce_fast_kernel(const uint16_t* __res
         run = -INFINITY;
         cur = S.shard[s];
       }
-      float lm = fmaxf(fmaxf(lo16(v[s][0]), hi16(v[s][0])), fmaxf(lo16(v[s][1]), hi16(v[s][1])));
-      lm = fmaxf(lm, fmaxf(fmaxf(lo16(v[s][2]), hi16(v[s][2])), fmaxf(lo16(v[s][3]), hi16(v[s][3]))));
-      run = fmaxf(run, lm);
+      run = fmaxf(run, vec_max(v[s]));
     }
     if (S.nslot > 0) {
       const float w = wave_max(run);
       if (lane == 0) red_max[wid][cur] = w;
     }
+  } else {
+    float run = -INFINITY;
+#pragma unroll
+    for (int s = 0; s < CE_SLOTS; ++s)
+      if (s < S.nslot) run = fmaxf(run, vec_max(v[s]));
+    const float w = wave_max(run);
+    if (lane == 0) red_max[wid][0] = w;
   }
   __syncthreads();
-  if (tid < S.P) {
+  if (STATS && tid < S.P) {
     float mr = -INFINITY;
     for (int w = 0; w < CE_NW; ++w) mr = fmaxf(mr, red_max[w][tid]);
     sh_m[tid] = mr;
   }
+  if (!STATS && tid == 0) {
+    float mr = -INFINITY;
+    for (int w = 0; w < CE_NW; ++w) mr = fmaxf(mr, red_max[w][0]);
+    sh_m[0] = mr;
+  }
   __syncthreads();
   float m = -INFINITY;
-  for (int r = 0; r < S.P; ++r) m = fmaxf(m, sh_m[r]);  // all-reduce(max)
+  for (int r = 0; r < (STATS ? S.P : 1); ++r) m = fmaxf(m, sh_m[r]);  // all-reduce(max)
   const float mL = m * LOG2E;
 
   // Per-shard sums s_r with the global maximum.  The target logit is read once
@@ -173,7 +192,7 @@ __global__ __launch_bounds__(CE_NT, 1) void ce_fast_kernel(const uint16_t* __res
 #pragma unroll
     for (int s = 0; s < CE_SLOTS; ++s) {
       if (s >= S.nslot) continue;
-      if (S.shard[s] != cur) {
+      if (STATS && S.shard[s] != cur) {
         const float w = wave_sum(run);
         if (lane == 0) red_sum[wid][cur] = w;
         run = 0.f;
@@ -188,23 +207,23 @@ __global__ __launch_bounds__(CE_NT, 1) void ce_fast_kernel(const uint16_t* __res
 #pragma unroll
       for (int q = 0; q < 4; ++q) v[s][q] = pack_f16(ex[2 * q], ex[2 * q + 1]);
     }
-    if (S.nslot > 0) {
+    if (S.nslot > 0 || !STATS) {
       const float w = wave_sum(run);
-      if (lane == 0) red_sum[wid][cur] = w;
+      if (lane == 0) red_sum[wid][STATS ? cur : 0] = w;
     }
   }
   __syncthreads();
-  if (tid < S.P) {
+  if (tid < (STATS ? S.P : 1)) {
     float sr = 0.f;
     for (int w = 0; w < CE_NW; ++w) sr += red_sum[w][tid];
     sh_s[tid] = sr;
   }
   __syncthreads();
   float ssum = 0.f;
-  for (int r = 0; r < S.P; ++r) ssum += sh_s[r];  // all-reduce(sum), rank order
+  for (int r = 0; r < (STATS ? S.P : 1); ++r) ssum += sh_s[r];  // all-reduce(sum), rank order
   const float t = y_ok ? zy - m : 0.f;  // the owning shard's target term
   if (tid == 0) row_loss[row] = logf(ssum) - t;
-  if (stats != nullptr && tid < S.P) {
+  if (STATS && tid < S.P) {
     const bool owns = y >= S.sbeg[tid] && y < S.sbeg[tid + 1];
     float* st = stats + (row * S.P + tid) * 3;
     st[0] = sh_m[tid];
@@ -227,8 +246,9 @@ __global__ __launch_bounds__(CE_NT, 1) void ce_fast_kernel(const uint16_t* __res
       float g[8];
 #pragma unroll
       for (int e = 0; e < 8; ++e) g[e] = f16_elem(v[s], e) * scale;
-      *reinterpret_cast<u32x4*>(dz + 8 * (int64_t)vi) =
-          u32x4{pack_bf16(g[0], g[1]), pack_bf16(g[2], g[3]), pack_bf16(g[4], g[5]), pack_bf16(g[6], g[7])};
+      __builtin_nontemporal_store(
+          u32x4{pack_bf16(g[0], g[1]), pack_bf16(g[2], g[3]), pack_bf16(g[4], g[5]), pack_bf16(g[6], g[7])},
+          reinterpret_cast<u32x4*>(dz + 8 * (int64_t)vi));
     }
   }
   if (owner) {
@@ -367,9 +387,14 @@ hipError_t launch_vocab_ce(const CeArgs& a, hipStream_t s) {
       }
     }
     if (fast) {
-      hipLaunchKernelGGL(ce_fast_kernel, dim3((unsigned)a.T), dim3(CE_NT), 0, s,
-                         static_cast<const uint16_t*>(a.logits), a.labels, static_cast<uint16_t*>(a.dlogits),
-                         a.row_loss, a.shard_stats, a.V, invT, S);
+      if (a.shard_stats != nullptr)
+        hipLaunchKernelGGL(ce_fast_kernel<true>, dim3((unsigned)a.T), dim3(CE_NT), 0, s,
+                           static_cast<const uint16_t*>(a.logits), a.labels, static_cast<uint16_t*>(a.dlogits),
+                           a.row_loss, a.shard_stats, a.V, invT, S);
+      else
+        hipLaunchKernelGGL(ce_fast_kernel<false>, dim3((unsigned)a.T), dim3(CE_NT), 0, s,
+                           static_cast<const uint16_t*>(a.logits), a.labels, static_cast<uint16_t*>(a.dlogits),
+                           a.row_loss, nullptr, a.V, invT, S);
     } else if (a.dtype == 1) {
       hipLaunchKernelGGL(ce_general_kernel<uint16_t>, dim3((unsigned)a.T), dim3(256), 0, s,
                          static_cast<const uint16_t*>(a.logits), a.labels, static_cast<uint16_t*>(a.dlogits),
