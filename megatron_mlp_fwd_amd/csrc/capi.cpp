@@ -253,7 +253,7 @@ int tp_mlp_fwd_bwd(int tp, int dtype, int w_layout, int64_t T, int64_t d, int64_
   hipStream_t s = static_cast<hipStream_t>(stream);
   const int64_t e = esize(dtype);
   char* wsb = static_cast<char*>(ws);
-  char* pre = wsb;                                            // T x f pre-activation, then dZ in place
+  char* pre = wsb;                                            // T x f GELU'(pre-activation), then dZ in place
   char* act = wsb + align256((size_t)(T * f * e));            // T x f activation
   const int64_t pstride = (int64_t)(align256((size_t)(T * d * 4)) / 4);
   float* zpart = reinterpret_cast<float*>(wsb + 2 * align256((size_t)(T * f * e)));
@@ -292,9 +292,10 @@ int tp_mlp_fwd_bwd(int tp, int dtype, int w_layout, int64_t T, int64_t d, int64_
   }
 
   hipError_t he;
-  // Forward fc1 (column-parallel GEMM, GELU epilogue); then fc2 (row-parallel
+  // Forward fc1 (column-parallel GEMM; its epilogue writes H = GELU(P) and
+  // GELU'(P), evaluated from the fp32 accumulator); then fc2 (row-parallel
   // GEMM) together with the two backward products that need only H and gy:
-  // dW2 and the activation gradient with the GELU' epilogue; then dW1 and dx.
+  // dW2 and dZ = (gy W2^T) * GELU'(P); then dW1 and dx.
   if ((he = run_jobs(fwd1, dtype, s)) != hipSuccess) return hip_fail(he, "fc1 GEMM");
   if ((he = run_jobs(mid, dtype, s)) != hipSuccess) return hip_fail(he, "fc2 / dW2 / dH GEMMs");
   if ((he = run_jobs(last, dtype, s)) != hipSuccess) return hip_fail(he, "dW1 / dx GEMMs");

@@ -18,7 +18,7 @@ struct GemmProb {
   const void* A;
   const void* B;
   void* C;
-  const void* aux_in;   // epilogue input (pre-activation for EPI_DGELU)
+  const void* aux_in;   // epilogue input (GELU'(pre-activation) for EPI_DGELU)
   void* aux_out;        // epilogue second output (activation for EPI_GELU)
   int64_t sa_m, sa_k, sb_k, sb_n, ldc;
   int M, N, K;
@@ -37,8 +37,8 @@ struct GemmBatch {
 
 enum Epilogue {
   EPI_F32 = 0,    // C (fp32) = acc
-  EPI_GELU = 1,   // C (compute dtype) = acc  [pre-activation], aux_out = gelu(acc)
-  EPI_DGELU = 2,  // C (compute dtype) = acc * gelu'(aux_in)    [in place allowed]
+  EPI_GELU = 1,   // C (compute dtype) = gelu'(acc), aux_out = gelu(acc)   [acc = pre-activation]
+  EPI_DGELU = 2,  // C (compute dtype) = acc * aux_in                       [in place allowed]
 };
 
 constexpr int gemm_kind(bool a_kmajor, bool b_kmajor, int epi) {

@@ -63,11 +63,7 @@ __device__ __forceinline__ PhiExp phi_exp(float x) {
   const float q = 0.5f * p * t * e;  // Phi(-|x|)
   return PhiExp{x >= 0.f ? 1.f - q : q, e};
 }
-__device__ __forceinline__ float gelu_f(float x) { return x * phi_exp(x).Phi; }
-__device__ __forceinline__ float gelu_prime_f(float x) {
-  const PhiExp r = phi_exp(x);
-  return fmaf(0.39894228040143268f * x, r.e, r.Phi);
-}
+
 
 // Workgroups are handed to the 8 XCDs round-robin; renumber so that each XCD
 // walks a contiguous range of tiles (neighbouring tiles share its L2).
@@ -97,7 +93,7 @@ __device__ __forceinline__ TileCoord locate_tile(const GemmBatch& batch) {
 }
 
 // Apply the epilogue to four consecutive outputs C[m][n .. n+3] (off = m*ldc+n).
-// For EPI_DGELU, `pre` holds the four bf16 pre-activations when the caller
+// For EPI_DGELU, `pre` holds the four bf16 values gelu'(P) when the caller
 // prefetched them (full vector rows); otherwise they are loaded here.
 template <int EPI>
 __device__ __forceinline__ void epilogue_store(const GemmProb& P, floatx4 v, int64_t off, int n, int N, int vec_c,
@@ -115,35 +111,39 @@ __device__ __forceinline__ void epilogue_store(const GemmProb& P, floatx4 v, int
         if (n + r < N) __builtin_nontemporal_store(v[r], c + r);
     }
   } else if constexpr (EPI == EPI_GELU) {
+    // acc is the pre-activation P: the activation H = gelu(P) is the next
+    // GEMM's operand and gelu'(P), evaluated here from the fp32 accumulator,
+    // is all the backward pass needs of P.
     uint16_t* c = static_cast<uint16_t*>(P.C) + off;
     uint16_t* h = static_cast<uint16_t*>(P.aux_out) + off;
-    floatx4 gv;
-    for (int r = 0; r < 4; ++r) gv[r] = gelu_f(v[r]);
+    floatx4 gv, dv;
+    for (int r = 0; r < 4; ++r) {
+      const PhiExp q = phi_exp(v[r]);
+      gv[r] = v[r] * q.Phi;
+      dv[r] = fmaf(0.39894228040143268f * v[r], q.e, q.Phi);
+    }
     if (full) {
-      *reinterpret_cast<u32x2*>(c) = u32x2{pack_bf16(v[0], v[1]), pack_bf16(v[2], v[3])};
+      *reinterpret_cast<u32x2*>(c) = u32x2{pack_bf16(dv[0], dv[1]), pack_bf16(dv[2], dv[3])};
       *reinterpret_cast<u32x2*>(h) = u32x2{pack_bf16(gv[0], gv[1]), pack_bf16(gv[2], gv[3])};
     } else {
       for (int r = 0; r < 4; ++r)
         if (n + r < N) {
-          c[r] = __builtin_bit_cast(uint16_t, (__bf16)v[r]);
+          c[r] = __builtin_bit_cast(uint16_t, (__bf16)dv[r]);
           h[r] = __builtin_bit_cast(uint16_t, (__bf16)gv[r]);
         }
     }
-  } else {  // EPI_DGELU: C = acc * gelu'(pre), pre read from aux_in (may alias C)
+  } else {  // EPI_DGELU: C = acc * gelu'(P), gelu'(P) read from aux_in (may alias C)
     uint16_t* c = static_cast<uint16_t*>(P.C) + off;
     if (full) {
-      v[0] *= gelu_prime_f(bf_lo(pre[0]));
-      v[1] *= gelu_prime_f(bf_hi(pre[0]));
-      v[2] *= gelu_prime_f(bf_lo(pre[1]));
-      v[3] *= gelu_prime_f(bf_hi(pre[1]));
+      v[0] *= bf_lo(pre[0]);
+      v[1] *= bf_hi(pre[0]);
+      v[2] *= bf_lo(pre[1]);
+      v[3] *= bf_hi(pre[1]);
       *reinterpret_cast<u32x2*>(c) = u32x2{pack_bf16(v[0], v[1]), pack_bf16(v[2], v[3])};
     } else {
       const uint16_t* p = static_cast<const uint16_t*>(P.aux_in) + off;
       for (int r = 0; r < 4; ++r)
-        if (n + r < N) {
-          const float x = __uint_as_float((uint32_t)p[r] << 16);
-          c[r] = __builtin_bit_cast(uint16_t, (__bf16)(v[r] * gelu_prime_f(x)));
-        }
+        if (n + r < N) c[r] = __builtin_bit_cast(uint16_t, (__bf16)(v[r] * __uint_as_float((uint32_t)p[r] << 16)));
     }
   }
 }
@@ -152,8 +152,7 @@ __device__ __forceinline__ void epilogue_store(const GemmProb& P, floatx4 v, int
 // wave).  Pass q moves MFMA blocks mi = 2q, 2q+1 of every wave (a 32 x TN_
 // region per wave) into LDS, then each wave reads its region back
 // row-contiguously and applies the epilogue with coalesced stores.  For
-// EPI_DGELU the pass's pre-activations are loaded before the LDS exchange so
-// their latency overlaps it.  The wave (wm, wn) owns rows wm*TM_ .. and
+// EPI_DGELU the tile's gelu'(P) values are loaded before the first exchange.  The wave (wm, wn) owns rows wm*TM_ .. and
 // columns wn*TN_ .. of the block tile, and acc[ni][mi] holds
 // C[m0 + wm*TM_ + mi*16 + lane%16][n0 + wn*TN_ + ni*16 + 4*(lane/16) + r].
 template <int EPI, int TM_, int TN_>
@@ -170,21 +169,25 @@ __device__ __forceinline__ void epilogue_via_lds(float* stage, const floatx4 (&a
   const int col = 4 * (lane % LANES_PER_ROW);
   const int n = n0 + wn * TN_ + col;
   const bool vec_n = vec_c && n + 3 < N;
-  // Passes are unrolled at compile time (static_for), so acc is only ever
-  // indexed by constants and stays in registers.
+  // For EPI_DGELU the whole tile's gelu'(P) values (TM_/32 passes x ITS
+  // loads per lane) are requested before the first pass, so their latency
+  // overlaps the LDS exchanges instead of stalling each pass.
+  constexpr int NPRE = EPI == EPI_DGELU ? (TM_ / 32) * ITS : 1;
+  u32x2 pre[NPRE];
+  if constexpr (EPI == EPI_DGELU) {
+#pragma unroll
+    for (int i = 0; i < NPRE; ++i) {
+      const int m = m0 + wm * TM_ + 32 * (i / ITS) + lane / LANES_PER_ROW + ROWS_PER_IT * (i % ITS);
+      pre[i] = (vec_n && m < M)
+                   ? *reinterpret_cast<const u32x2*>(static_cast<const uint16_t*>(P.aux_in) + (int64_t)m * ldc + n)
+                   : u32x2{0u, 0u};
+    }
+  }
+  // Passes are unrolled at compile time (static_for), so acc and pre are
+  // only ever indexed by constants and stay in registers.
   static_for<0, TM_ / 32>([&](auto q_) {
     constexpr int q = decltype(q_)::value;
     const int mbase = m0 + wm * TM_ + 32 * q + lane / LANES_PER_ROW;
-    u32x2 pre[ITS];
-    if constexpr (EPI == EPI_DGELU) {
-#pragma unroll
-      for (int it = 0; it < ITS; ++it) {
-        const int m = mbase + ROWS_PER_IT * it;
-        pre[it] = (vec_n && m < M)
-                      ? *reinterpret_cast<const u32x2*>(static_cast<const uint16_t*>(P.aux_in) + (int64_t)m * ldc + n)
-                      : u32x2{0u, 0u};
-      }
-    }
 #pragma unroll
     for (int h = 0; h < 2; ++h)
 #pragma unroll
@@ -199,7 +202,7 @@ __device__ __forceinline__ void epilogue_via_lds(float* stage, const floatx4 (&a
       if (m < M && n < N) {
         const floatx4 v = *reinterpret_cast<const floatx4*>(ep + row * LD + col);
         if constexpr (EPI == EPI_DGELU)
-          epilogue_store<EPI>(P, v, (int64_t)m * ldc + n, n, N, vec_c, pre[it]);
+          epilogue_store<EPI>(P, v, (int64_t)m * ldc + n, n, N, vec_c, pre[q * ITS + it]);
         else
           epilogue_store<EPI>(P, v, (int64_t)m * ldc + n, n, N, vec_c);
       }

@@ -80,12 +80,11 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(const GemmBatch batch, in
       const float v = acc[i][j];
       if constexpr (EPI == EPI_F32) {
         static_cast<float*>(P.C)[off] = v;
-      } else if constexpr (EPI == EPI_GELU) {
-        static_cast<float*>(P.C)[off] = v;
+      } else if constexpr (EPI == EPI_GELU) {  // v is the pre-activation
+        static_cast<float*>(P.C)[off] = gelu_prime_f(v);
         static_cast<float*>(P.aux_out)[off] = gelu_f(v);
-      } else {
-        const float pre = static_cast<const float*>(P.aux_in)[off];
-        static_cast<float*>(P.C)[off] = v * gelu_prime_f(pre);
+      } else {  // aux_in holds gelu'(pre-activation)
+        static_cast<float*>(P.C)[off] = v * static_cast<const float*>(P.aux_in)[off];
       }
     }
   }
