@@ -195,16 +195,19 @@ __device__ __forceinline__ void epilogue_via_lds(float* stage, const floatx4 (&a
         *reinterpret_cast<floatx4*>(ep + (h * 16 + (lane & 15)) * LD + ni * 16 + 4 * (lane >> 4)) =
             acc[ni][2 * q + h];
     __syncthreads();
+    // All of the pass's LDS reads first (one wait), then the math and stores.
+    floatx4 vals[ITS];
+#pragma unroll
+    for (int it = 0; it < ITS; ++it)
+      vals[it] = *reinterpret_cast<const floatx4*>(ep + (ROWS_PER_IT * it + lane / LANES_PER_ROW) * LD + col);
 #pragma unroll
     for (int it = 0; it < ITS; ++it) {
-      const int row = ROWS_PER_IT * it + lane / LANES_PER_ROW;
       const int m = mbase + ROWS_PER_IT * it;
       if (m < M && n < N) {
-        const floatx4 v = *reinterpret_cast<const floatx4*>(ep + row * LD + col);
         if constexpr (EPI == EPI_DGELU)
-          epilogue_store<EPI>(P, v, (int64_t)m * ldc + n, n, N, vec_c, pre[q * ITS + it]);
+          epilogue_store<EPI>(P, vals[it], (int64_t)m * ldc + n, n, N, vec_c, pre[q * ITS + it]);
         else
-          epilogue_store<EPI>(P, v, (int64_t)m * ldc + n, n, N, vec_c);
+          epilogue_store<EPI>(P, vals[it], (int64_t)m * ldc + n, n, N, vec_c);
       }
     }
     __syncthreads();
