@@ -257,6 +257,141 @@ __global__ __launch_bounds__(CE_NT, 1) void ce_fast_kernel(const uint16_t* __res
   }
 }
 
+
+// ---------------------------------------------------------------- paired path
+// Rows without per-shard statistics, bf16: two 512-thread workgroups per CU,
+// each holding its whole row: CP_RS 16-byte slots per thread in registers
+// (88 VGPRs) and the remainder in LDS (filled by buffer_load ... lds, so no
+// register staging).  With two rows resident per CU, one row's arithmetic
+// overlaps the other's loads and stores, which a single register-resident row
+// per CU cannot do.  Same arithmetic as ce_fast_kernel<false>.
+constexpr int CP_NT = 512;
+constexpr int CP_NW = CP_NT / 64;
+constexpr int CP_RS = 22;           // register slots per thread
+constexpr int CP_LDS_VEC = 4864;    // LDS capacity in 16-byte vectors (76 KB)
+constexpr uint32_t CP_OOB = 0x80000000u;
+
+__global__ __launch_bounds__(CP_NT) __attribute__((amdgpu_waves_per_eu(4, 4))) void ce_pair_kernel(const uint16_t* __restrict__ logits,
+                                                            const int64_t* __restrict__ labels,
+                                                            uint16_t* __restrict__ dlogits, float* __restrict__ row_loss,
+                                                            int64_t V, float invT) {
+  __shared__ __attribute__((aligned(1024))) u32x4 part[CP_LDS_VEC];
+  __shared__ float red[CP_NW];
+  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+  const int64_t row = blockIdx.x;
+  const int nvec = (int)(V / 8);
+  const int nreg = nvec < CP_RS * CP_NT ? nvec : CP_RS * CP_NT;  // vectors held in registers
+  const int nlds = nvec - nreg;                                  // vectors held in LDS
+  const __amdgpu_buffer_rsrc_t rz =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(logits + row * V), (short)0, (int)(V * 2), 0x00020000);
+  const __amdgpu_buffer_rsrc_t rd =
+      __builtin_amdgcn_make_buffer_rsrc(dlogits + row * V, (short)0, (int)(V * 2), 0x00020000);
+  const int64_t y = labels[row];
+
+  // LDS part: wave instruction j moves vectors nreg + 64 j .. + 63 (lanes past
+  // the row end read zeros and are never used).
+  for (int j = wid; 64 * j < nlds; j += CP_NW)
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rz, (__attribute__((address_space(3))) void*)&part[64 * j], 16,
+                                             (uint32_t)(16 * (nreg + 64 * j + lane)), 0, 0, 2);
+  // Register part: slot s of thread tid holds vector s * CP_NT + tid.
+  // Lanes past the row end load zeros (out of range) and are skipped below.
+  u32x4 v[CP_RS];
+#pragma unroll
+  for (int s = 0; s < CP_RS; ++s) {
+    const int i = s * CP_NT + tid;
+    v[s] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                                         rz, i < nreg ? (uint32_t)(16 * i) : CP_OOB, 0, 2));
+  }
+  __builtin_amdgcn_s_waitcnt(0);  // this wave's DMA into LDS has landed
+  __syncthreads();
+
+  // Row maximum.
+  float run = -INFINITY;
+#pragma unroll
+  for (int s = 0; s < CP_RS; ++s)
+    if (s * CP_NT + tid < nreg) run = fmaxf(run, vec_max(v[s]));
+  for (int j = tid; j < nlds; j += CP_NT) run = fmaxf(run, vec_max(part[j]));
+  {
+    const float w = wave_max(run);
+    if (lane == 0) red[wid] = w;
+  }
+  __syncthreads();
+  float m = red[0];
+  for (int w = 1; w < CP_NW; ++w) m = fmaxf(m, red[w]);
+  const float mL = m * LOG2E;
+  __syncthreads();  // red is reused for the sums
+  // Opaque to the compiler: otherwise it keeps the max pass's widened logits
+  // alive for the exp pass, which needs far more registers than the row.
+#pragma unroll
+  for (int s = 0; s < CP_RS; ++s) asm volatile("" : "+v"(v[s]));
+  int t2 = tid;  // likewise for the per-slot offsets and masks derived from tid
+  asm volatile("" : "+v"(t2));
+
+  // exp(z - m) once per logit, summed in fp32 and kept as fp16 in place.
+  const bool y_ok = y >= 0 && y < V;
+  const float zy = y_ok ? __uint_as_float((uint32_t)logits[row * V + (y_ok ? y : 0)] << 16) : 0.f;
+  float sum = 0.f;
+  auto expv = [&](u32x4& x) {
+    float ex[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) ex[e] = __builtin_amdgcn_exp2f(elem(x, e) * LOG2E - mL);
+    sum += ((ex[0] + ex[1]) + (ex[2] + ex[3])) + ((ex[4] + ex[5]) + (ex[6] + ex[7]));
+#pragma unroll
+    for (int q = 0; q < 4; ++q) x[q] = pack_f16(ex[2 * q], ex[2 * q + 1]);
+  };
+  // (the scheduling fences keep the compiler from overlapping slots, which
+  // would need registers the 88 data registers leave no room for)
+#pragma unroll
+  for (int s = 0; s < CP_RS; ++s) {
+    if (s * CP_NT + t2 < nreg) expv(v[s]);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  for (int j = tid; j < nlds; j += CP_NT) {
+    u32x4 x = part[j];
+    expv(x);
+    part[j] = x;  // the same thread reads it back in the gradient pass
+  }
+  {
+    const float w = wave_sum(sum);
+    if (lane == 0) red[wid] = w;
+  }
+  __syncthreads();
+  float ssum = red[0];
+  for (int w = 1; w < CP_NW; ++w) ssum += red[w];
+  if (tid == 0) row_loss[row] = logf(ssum) - (y_ok ? zy - m : 0.f);
+
+  // Gradient, written once; the lane that wrote the vector holding the
+  // target rewrites that element afterwards (program order).
+  const float scale = invT / ssum;
+  const int vy = y_ok ? (int)(y >> 3) : -1;
+  auto grad = [&](const u32x4& x, int i) {
+    float g[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) g[e] = f16_elem(x, e) * scale;
+    const u32x4 w{pack_bf16(g[0], g[1]), pack_bf16(g[2], g[3]), pack_bf16(g[4], g[5]), pack_bf16(g[6], g[7])};
+    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(__attribute__((ext_vector_type(4))) int, w), rd,
+                                           (uint32_t)(16 * i), 0, 2);
+  };
+  bool owner = false;
+#pragma unroll
+  for (int s = 0; s < CP_RS; ++s) {
+    const int i = s * CP_NT + t2;
+    if (i < nreg) {
+      owner |= i == vy;
+      grad(v[s], i);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  for (int j = tid; j < nlds; j += CP_NT) {
+    owner |= nreg + j == vy;
+    grad(part[j], nreg + j);
+  }
+  if (owner) {
+    const float gy = __builtin_amdgcn_exp2f(zy * LOG2E - mL) * scale - invT;
+    dlogits[row * V + y] = __builtin_bit_cast(uint16_t, (__bf16)gy);
+  }
+}
+
 // ---------------------------------------------------------------- general path
 template <typename T>
 __device__ __forceinline__ float ld_logit(const T* p, int64_t j);
@@ -386,7 +521,16 @@ hipError_t launch_vocab_ce(const CeArgs& a, hipStream_t s) {
         }
       }
     }
-    if (fast) {
+    // Without per-shard statistics the shard layout does not matter: the
+    // paired kernel takes any bf16 row that fits its registers + LDS.
+    const int64_t nvec = a.V / 8, nlds = nvec - (nvec < CP_RS * CP_NT ? nvec : CP_RS * CP_NT);
+    const bool pair = a.dtype == 1 && a.shard_stats == nullptr && a.V % 8 == 0 && aligned16(a.logits) &&
+                      aligned16(a.dlogits) && (nlds + 63) / 64 * 64 <= CP_LDS_VEC;
+    if (pair) {
+      hipLaunchKernelGGL(ce_pair_kernel, dim3((unsigned)a.T), dim3(CP_NT), 0, s,
+                         static_cast<const uint16_t*>(a.logits), a.labels, static_cast<uint16_t*>(a.dlogits),
+                         a.row_loss, a.V, invT);
+    } else if (fast) {
       if (a.shard_stats != nullptr)
         hipLaunchKernelGGL(ce_fast_kernel<true>, dim3((unsigned)a.T), dim3(CE_NT), 0, s,
                            static_cast<const uint16_t*>(a.logits), a.labels, static_cast<uint16_t*>(a.dlogits),

@@ -266,24 +266,46 @@ def test_mlp_llama3_70b_tp8_rank_sampled(tpr):
 
 # ---------------------------------------------------------------- vocab CE
 
+@pytest.mark.parametrize("stats", [True, False])
 @pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
 @pytest.mark.parametrize("V,parts", [(8, 1), (8, 3), (1001, 3), (4096, 8), (4096, 17), (40000, 8), (100, 5000),
                                      (128256, 8)])
-def test_ce_small(tpr, V, parts, dtype):
-    say("vocab CE", V, parts, dtype)
+def test_ce_small(tpr, V, parts, dtype, stats):
+    say("vocab CE", V, parts, dtype, "stats" if stats else "no stats")
     T = 5
     logits, labels = workloads.vocab_ce(T=T, V=V, seed=V + parts, device=DEV, dtype=dtype)
-    loss, dl, st = tpr.vocab_parallel_ce_fwd_bwd(parts, logits, labels, shard_stats=True)
+    loss, dl, st = tpr.vocab_parallel_ce_fwd_bwd(parts, logits, labels, shard_stats=stats)
     torch.cuda.synchronize()
     z, y = f64(logits), labels.cpu().numpy()
     wl, _, wg, wst = oracle.vocab_parallel_ce(z, y, parts)
     tol = tol_of(dtype)
     assert abs(loss.item() - wl) <= tol * abs(wl)
     assert rel_err(f64(dl), wg) <= tol
+    if not stats:
+        assert st is None
+        return
     gst = f64(st)
     np.testing.assert_array_equal(gst[:, :, 0], wst[:, :, 0])           # maxima are exact
     np.testing.assert_allclose(gst[:, :, 1], wst[:, :, 1], rtol=1e-5, atol=1e-30)
     np.testing.assert_allclose(gst[:, :, 2], wst[:, :, 2], rtol=1e-6, atol=1e-6)
+
+
+# Rows held partly in registers (22 x 512 vectors of 8 logits) and partly in
+# LDS (up to 4864 vectors): empty, single-vector, ragged and full LDS parts,
+# and one vector past the capacity (served by the single-row kernel).
+@pytest.mark.parametrize("V", [8 * 11264, 8 * 11265, 8 * 11364, 8 * (11264 + 4864), 8 * (11264 + 4864) + 8])
+def test_ce_bf16_row_split_edges(tpr, V):
+    say("vocab CE bf16, no stats, V =", V)
+    T = 4
+    logits, labels = workloads.vocab_ce(T=T, V=V, seed=V, device=DEV)
+    labels[0] = V - 1   # target in the last vector
+    labels[1] = 0
+    loss, dl, _ = tpr.vocab_parallel_ce_fwd_bwd(4, logits, labels)
+    torch.cuda.synchronize()
+    z, y = f64(logits), labels.cpu().numpy()
+    wl, _, wg = oracle.cross_entropy(z, y, grad_rows=np.arange(T))
+    assert abs(loss.item() - wl) <= 1e-5 * abs(wl)
+    assert rel_err(f64(dl), wg) <= TOL_BF16
 
 
 def test_ce_zero_rows(tpr):
@@ -318,6 +340,24 @@ def test_ce_full_config(tpr):
     np.testing.assert_array_equal(gst[:, :, 0], wst[:, :, 0])
     np.testing.assert_allclose(gst[:, :, 1], wst[:, :, 1], rtol=1e-5)
     np.testing.assert_allclose(gst[:, :, 2], wst[:, :, 2], rtol=1e-6, atol=1e-6)
+
+
+def test_ce_full_config_no_stats(tpr):
+    # The benchmarked call: 4096 x 128256, 8 shards, no per-shard statistics.
+    say("vocab CE 4096 x 128256 bf16, 8 shards, no stats")
+    T, V, P = 4096, 128256, 8
+    logits, labels = workloads.vocab_ce(T=T, V=V, seed=0, device=DEV)
+    loss, dl, st = tpr.vocab_parallel_ce_fwd_bwd(P, logits, labels)
+    torch.cuda.synchronize()
+    assert st is None
+    rowsum = dl.float().sum(dim=1)
+    assert rowsum.abs().max().item() <= 2.0 ** -7 / T
+    z = logits.float().cpu().numpy()
+    y = labels.cpu().numpy()
+    rows = np.sort(np.random.default_rng(1).choice(T, 16, replace=False))
+    wl, _, wg = oracle.cross_entropy(z, y, grad_rows=rows)
+    assert abs(loss.item() - wl) <= 1e-5 * abs(wl)
+    assert rel_err(f64(dl[rows]), wg) <= TOL_BF16
 
 
 def test_determinism(tpr):
