@@ -107,10 +107,10 @@ int sharded_matmul_fwd_bwd(int axis, int parts, int dtype, int64_t M, int64_t K,
 
 /* ---- column-then-row tensor-parallel GELU MLP ------------------------- */
 /*
- * Bytes of workspace tp_mlp_fwd_bwd() needs: the pre-activation and the
- * activation (T x f each, in `dtype`; the pre-activation buffer is reused
- * for the gradient at the pre-activation), plus, when tp > 1, the tp
- * full-shape fp32 partials of y and of dx.  Returns 0 for invalid arguments.
+ * Bytes of workspace tp_mlp_fwd_bwd() needs: gelu' of the pre-activation
+ * and the activation (T x f each, in `dtype`; the first buffer is reused for
+ * the gradient at the pre-activation), plus, when tp > 1, the tp full-shape
+ * fp32 partials of y and of dx.  Returns 0 for invalid arguments.
  */
 size_t tp_mlp_workspace_bytes(int tp, int dtype, int64_t T, int64_t d, int64_t f);
 
@@ -118,7 +118,8 @@ size_t tp_mlp_workspace_bytes(int tp, int dtype, int64_t T, int64_t d, int64_t f
  * [TP] 2.A and [CARDS] 01 / 02: `tp` ranks each own hidden columns [lo, hi)
  * of W1 (column-parallel) and the same rows of W2 (row-parallel).  Per rank,
  *   forward:  P_r = x W1_r;  H_r = gelu(P_r) (exact erf, fused in the GEMM
- *             epilogue);  Z_r = H_r W2_r, a full-shape T x d partial;
+ *             epilogue, which also keeps gelu'(P_r) for the backward);
+ *             Z_r = H_r W2_r, a full-shape T x d partial;
  *   backward (L = sum(y * gy), the same gy used once by every rank):
  *             dW2_r = H_r^T gy;  dZ_r = (gy W2_r^T) * gelu'(P_r) (fused);
  *             dW1_r = x^T dZ_r;  dx_r = dZ_r W1_r^T;
@@ -126,8 +127,8 @@ size_t tp_mlp_workspace_bytes(int tp, int dtype, int64_t T, int64_t d, int64_t f
  * fixed rank order).  With tp == 1 the call computes one rank's share: pass
  * the rank's weight shards (w1 d x f_r, w2 f_r x d in TPR_W_MATH) and y, dx
  * are that rank's partials Z_r, dx_r.  For TPR_BF16 the activation and the
- * pre-activation gradient are rounded to bf16 (they are GEMM operands); the
- * pre-activation is kept in bf16.
+ * pre-activation gradient are rounded to bf16 (they are GEMM operands), and
+ * so is the kept gelu'(P_r).
  *   x, gy: T x d in `dtype` (leading dims of an activation flatten into T);
  *   w1, w2: weights in `dtype` and `w_layout`;
  *   y, dx: fp32 T x d;  dw1, dw2: fp32, same shapes/layout as w1, w2.

@@ -15,7 +15,10 @@ it cites:
   then row MLP, its backward equations and the vocabulary-sharded
   cross-entropy equations;
 * "第 6 课：张量并行 TP" (TP lesson page) -- column-parallel and row-parallel
-  linears, the block-GEMM identity and the GELU MLP composed from them.
+  linears, the block-GEMM identity and the GELU MLP composed from them;
+* the multi-card tensor page's vocabulary-split output head (``head.py``):
+  logits per vocabulary shard, the sharded cross-entropy, and the hidden
+  state's gradient summed across the shards.
 
 Where a method reaches a result that has a plain definition (the unsharded
 product, the unsharded MLP, the unsharded cross-entropy), the oracle used for
@@ -31,10 +34,12 @@ from .sharding import shard_range, shard_ranges
 from .matmul import AXES, check_matmul_args, matmul_grads, sharded_matmul, sharded_matmul_partials
 from .mlp import gelu, gelu_prime, to_math_layout, mlp_fwd_bwd, tp_mlp_fwd_bwd, mlp_sampled
 from .ce import cross_entropy, vocab_parallel_ce
+from .head import head_ce, vocab_parallel_head_ce
 
 __all__ = [
     "shard_range", "shard_ranges",
     "AXES", "check_matmul_args", "matmul_grads", "sharded_matmul", "sharded_matmul_partials",
     "gelu", "gelu_prime", "to_math_layout", "mlp_fwd_bwd", "tp_mlp_fwd_bwd", "mlp_sampled",
     "cross_entropy", "vocab_parallel_ce",
+    "head_ce", "vocab_parallel_head_ce",
 ]
