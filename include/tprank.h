@@ -8,6 +8,7 @@
  *           sections 题意与假设 (assumptions) and 解题路线 (solution route)
  *   [CARDS] "多卡张量：拆开计算，再合回同一结果"
  *           sections 01 / COLUMN THEN ROW, 02 / BACKWARD, 04 / VOCABULARY SHARDS
+ *           (and the output-head paragraph after section 04's tables)
  *   [TP]    "第 6 课：张量并行 TP"
  *           section 1 (column- and row-parallel linears) and 2.A (the MLP)
  *
@@ -171,6 +172,39 @@ int vocab_parallel_ce_fwd_bwd(int parts, int dtype, int64_t T, int64_t V,
                               const void* logits, const int64_t* labels,
                               float* loss, void* dlogits, float* shard_stats,
                               void* ws, size_t ws_bytes, void* stream);
+
+/* ---- vocabulary-parallel output head with cross-entropy --------------- */
+/*
+ * Bytes of workspace vocab_parallel_head_ce_fwd_bwd() needs: the logits and
+ * their gradient (T x V each, in `dtype`), the T per-row losses (fp32) and,
+ * when parts > 1, the parts full-shape fp32 partials of dh (T x d).  Returns
+ * 0 for invalid arguments.
+ */
+size_t vocab_parallel_head_ce_workspace_bytes(int parts, int dtype, int64_t T, int64_t d, int64_t V);
+
+/*
+ * [CARDS] 04 / VOCABULARY SHARDS and the paragraph after its tables: the
+ * output head split by vocabulary columns.  Rank r holds the columns V_r of
+ * the head matrix W (d x V) and computes
+ *     logits_r = h W_r              (T x V_r, kept in `dtype`),
+ * the ranks' cross-entropy statistics are combined exactly as in
+ * vocab_parallel_ce_fwd_bwd() (mean over the T positions), then
+ *     dW_r = h^T dlogits_r          (its columns of dW, in place),
+ *     dh   = sum_r dlogits_r W_r^T  (the shared hidden state's gradient,
+ *                                    summed across the shards in rank order).
+ * For TPR_BF16 the logits and dlogits are rounded to bf16 (as the CE entry
+ * point's inputs and outputs are); products accumulate in fp32.
+ *   h: T x d in `dtype`;  w: the head in `dtype`, d x V for TPR_W_MATH or the
+ *   (V, d) weight of a d -> V linear layer for TPR_W_TORCH;
+ *   labels: T int64 with 0 <= y < V (same contract as the CE entry point);
+ *   loss: one fp32 on the device;  dh: fp32 T x d;  dw: fp32, same shape and
+ *   layout as w.  T == 0 writes loss = 0 and zeroes dw.
+ * Errors: SHAPE, PARTITION, DTYPE (dtype or w_layout), NULLPTR, WORKSPACE, HIP.
+ */
+int vocab_parallel_head_ce_fwd_bwd(int parts, int dtype, int w_layout, int64_t T, int64_t d, int64_t V,
+                                   const void* h, const void* w, const int64_t* labels,
+                                   float* loss, float* dh, float* dw,
+                                   void* ws, size_t ws_bytes, void* stream);
 
 /* Message for the last non-zero status returned on the calling thread. */
 const char* tprank_last_error(void);

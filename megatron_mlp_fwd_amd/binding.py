@@ -31,6 +31,9 @@ _SIGS = {
     "tp_mlp_fwd_bwd": (_i32, [_i32, _i32, _i32, _i64, _i64, _i64, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
     "vocab_parallel_ce_workspace_bytes": (_sz, [_i32, _i64, _i64]),
     "vocab_parallel_ce_fwd_bwd": (_i32, [_i32, _i32, _i64, _i64, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
+    "vocab_parallel_head_ce_workspace_bytes": (_sz, [_i32, _i32, _i64, _i64, _i64]),
+    "vocab_parallel_head_ce_fwd_bwd": (_i32, [_i32, _i32, _i32, _i64, _i64, _i64, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
+                                              _sz, _vp]),
     "tprank_last_error": (ctypes.c_char_p, []),
 }
 
@@ -214,3 +217,40 @@ def vocab_parallel_ce_fwd_bwd(parts, logits, labels, shard_stats=False, out=None
         _check(lib.vocab_parallel_ce_fwd_bwd(parts, DTYPES[dt], T, V, _ptr(logits), _ptr(labels), loss.data_ptr(),
                                              _ptr(dlogits), _ptr(stats), _ptr(ws), wsb, _stream(stream)))
     return loss, dlogits, stats
+
+
+def vocab_parallel_head_ce_workspace_bytes(parts, dtype, T, d, V):
+    return load_library().vocab_parallel_head_ce_workspace_bytes(parts, DTYPES[dtype], T, d, V)
+
+
+def vocab_parallel_head_ce_fwd_bwd(parts, h, w, labels, w_layout="math", out=None, workspace=None, stream=None):
+    """Vocabulary-parallel output head (``parts`` shards of the vocabulary
+    columns of the head ``w``) followed by the mean cross-entropy, forward and
+    backward.  ``h`` is T x d; ``w`` is d x V ("math") or V x d ("torch").
+    Returns (loss: 0-d fp32 tensor, dh: fp32 like h, dw: fp32 like w)."""
+    lib = load_library()
+    layout = W_LAYOUTS[w_layout]
+    dt = h.dtype
+    if dt not in DTYPES:
+        raise ValueError(f"unsupported dtype {dt}")
+    if h.dim() != 2 or w.dim() != 2:
+        raise ValueError("h and w must be 2-D")
+    T, d = h.shape
+    V = w.shape[1] if layout == 0 else w.shape[0]
+    wshape = (d, V) if layout == 0 else (V, d)
+    dev = h.device
+    _need(h, "h", (T, d), dt, dev)
+    _need(w, "w", wshape, dt, dev)
+    _need(labels, "labels", (T,), torch.int64, dev)
+    if out is None:
+        out = (torch.empty((), device=dev), torch.empty(T, d, device=dev), torch.empty(wshape, device=dev))
+    loss, dh, dw = out
+    _need(loss, "loss", (), torch.float32, dev)
+    _need(dh, "dh", (T, d), torch.float32, dev)
+    _need(dw, "dw", wshape, torch.float32, dev)
+    ws, wsb = _workspace(lib.vocab_parallel_head_ce_workspace_bytes(parts, DTYPES[dt], T, d, V), dev, workspace)
+    with torch.cuda.device(dev):
+        _check(lib.vocab_parallel_head_ce_fwd_bwd(parts, DTYPES[dt], layout, T, d, V, _ptr(h), _ptr(w), _ptr(labels),
+                                                  loss.data_ptr(), _ptr(dh), _ptr(dw), _ptr(ws), wsb,
+                                                  _stream(stream)))
+    return loss, dh, dw

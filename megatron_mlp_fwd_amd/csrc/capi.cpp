@@ -341,4 +341,85 @@ int vocab_parallel_ce_fwd_bwd(int parts, int dtype, int64_t T, int64_t V, const 
   return TPR_OK;
 }
 
+// ---------------------------------------------------------------- vocab head + CE
+size_t vocab_parallel_head_ce_workspace_bytes(int parts, int dtype, int64_t T, int64_t d, int64_t V) {
+  if (parts < 1 || !dtype_ok(dtype) || T < 0 || d < 0 || V < 0) return 0;
+  size_t b = 2 * align256((size_t)(T * V * esize(dtype)));  // logits, dlogits
+  b += vocab_parallel_ce_workspace_bytes(parts, T, V);       // per-row losses
+  if (parts > 1) b += (size_t)parts * align256((size_t)(T * d * 4));  // dh partials
+  return b;
+}
+
+int vocab_parallel_head_ce_fwd_bwd(int parts, int dtype, int w_layout, int64_t T, int64_t d, int64_t V,
+                                   const void* h, const void* w, const int64_t* labels, float* loss, float* dh,
+                                   float* dw, void* ws, size_t ws_bytes, void* stream) {
+  if (!dim_ok(T) || !dim_ok(d) || !dim_ok(V) || V / 8 > INT_MAX)
+    return fail(TPR_ERR_SHAPE, "T, d, V must be in [0, 2^31) (got %lld, %lld, %lld)", (long long)T, (long long)d,
+                (long long)V);
+  if (T > 0 && V == 0) return fail(TPR_ERR_SHAPE, "V must be >= 1 when T > 0");
+  if (parts < 1) return fail(TPR_ERR_PARTITION, "parts must be >= 1 (got %d)", parts);
+  if (!dtype_ok(dtype)) return fail(TPR_ERR_DTYPE, "unknown dtype %d", dtype);
+  if (w_layout != TPR_W_MATH && w_layout != TPR_W_TORCH) return fail(TPR_ERR_DTYPE, "unknown w_layout %d", w_layout);
+  if (loss == nullptr || (T > 0 && labels == nullptr) || (T * d > 0 && (h == nullptr || dh == nullptr)) ||
+      (d * V > 0 && (w == nullptr || dw == nullptr)))
+    return fail(TPR_ERR_NULLPTR, "a required input or output pointer is NULL");
+  const size_t need = vocab_parallel_head_ce_workspace_bytes(parts, dtype, T, d, V);
+  if (ws_bytes < need || (need > 0 && ws == nullptr))
+    return fail(TPR_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", need, ws_bytes);
+
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const int64_t e = esize(dtype);
+  char* wsb = static_cast<char*>(ws);
+  char* logits = wsb;
+  char* dl = wsb + align256((size_t)(T * V * e));
+  float* row_loss = reinterpret_cast<float*>(wsb + 2 * align256((size_t)(T * V * e)));
+  float* slots = reinterpret_cast<float*>(reinterpret_cast<char*>(row_loss) + align256((size_t)T * 4));
+  const int64_t stride = (int64_t)(align256((size_t)(T * d * 4)) / 4);
+  const bool direct = parts == 1;
+  const bool math = w_layout == TPR_W_MATH;
+  int nslots = 0;
+  std::vector<Job> fwd, bwd;
+
+  for (int r = 0; r < parts; ++r) {
+    int64_t lo, hi;
+    shard_of(V, parts, r, &lo, &hi);
+    const int64_t n = hi - lo;
+    if (n == 0) continue;
+    // Rank r's head columns W_r (d x n): math w is d x V, torch w is V x d.
+    const char* wr = math ? cb(w) + lo * e : cb(w) + lo * d * e;
+    const int64_t wk = math ? V : 1, wn = math ? 1 : d;  // W_r(k, j) = wr[k * wk + j * wn]
+    // logits_r = h W_r (in the compute dtype), landing in its column slice.
+    fwd.push_back(job(prob(h, d, 1, wr, wk, wn, logits + lo * e, V, T, n, d), true, !math,
+                      dtype == TPR_BF16 ? tpr::EPI_BF16 : tpr::EPI_F32));
+    // dW_r = h^T dlogits_r (math, d x n) or its transpose (torch, n x d), in place.
+    if (math)
+      bwd.push_back(job(prob(h, 1, d, dl + lo * e, V, 1, dw + lo, V, d, n, T), false, false, tpr::EPI_F32));
+    else
+      bwd.push_back(job(prob(dl + lo * e, 1, V, h, d, 1, dw + lo * d, d, n, d, T), false, false, tpr::EPI_F32));
+    // dh_r = dlogits_r W_r^T, a full-shape partial: W_r^T(j, k) = W_r(k, j).
+    float* dst = direct ? dh : slots + nslots * stride;
+    bwd.push_back(job(prob(dl + lo * e, V, 1, wr, wn, wk, dst, d, T, d, n), true, math, tpr::EPI_F32));
+    ++nslots;
+  }
+
+  hipError_t he;
+  if ((he = run_jobs(fwd, dtype, s)) != hipSuccess) return hip_fail(he, "logits GEMMs");
+  tpr::CeArgs a{};
+  a.logits = logits;
+  a.labels = labels;
+  a.dlogits = dl;
+  a.shard_stats = nullptr;
+  a.row_loss = row_loss;
+  a.loss = loss;
+  a.T = T;
+  a.V = V;
+  a.parts = parts;
+  a.dtype = dtype;
+  if ((he = tpr::launch_vocab_ce(a, s)) != hipSuccess) return hip_fail(he, "vocab CE launch");
+  if ((he = run_jobs(bwd, dtype, s)) != hipSuccess) return hip_fail(he, "dW / dh GEMMs");
+  // The shared hidden state's gradient, summed across the vocabulary shards.
+  if ((he = finish_sum(dh, T, d, slots, nslots, stride, direct, s)) != hipSuccess) return hip_fail(he, "dh reduction");
+  return TPR_OK;
+}
+
 }  // extern "C"

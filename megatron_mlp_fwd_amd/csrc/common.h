@@ -39,6 +39,7 @@ enum Epilogue {
   EPI_F32 = 0,    // C (fp32) = acc
   EPI_GELU = 1,   // C (compute dtype) = gelu'(acc), aux_out = gelu(acc)   [acc = pre-activation]
   EPI_DGELU = 2,  // C (compute dtype) = acc * aux_in                       [in place allowed]
+  EPI_BF16 = 3,   // C (bf16) = acc, rounded to nearest even
 };
 
 constexpr int gemm_kind(bool a_kmajor, bool b_kmajor, int epi) {

@@ -190,6 +190,7 @@ hipError_t launch_epi(const GemmBatch& b, int epi, int vec_c, hipStream_t s) {
   switch (epi) {
     case EPI_F32: hipLaunchKernelGGL((gemm_bf16_kernel<AK, BKM, VEC, EPI_F32>), grid, block, 0, s, b, vec_c); break;
     case EPI_GELU: hipLaunchKernelGGL((gemm_bf16_kernel<AK, BKM, VEC, EPI_GELU>), grid, block, 0, s, b, vec_c); break;
+    case EPI_BF16: hipLaunchKernelGGL((gemm_bf16_kernel<AK, BKM, VEC, EPI_BF16>), grid, block, 0, s, b, vec_c); break;
     default: hipLaunchKernelGGL((gemm_bf16_kernel<AK, BKM, VEC, EPI_DGELU>), grid, block, 0, s, b, vec_c); break;
   }
   return hipGetLastError();

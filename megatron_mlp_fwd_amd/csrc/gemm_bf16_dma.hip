@@ -372,6 +372,8 @@ __global__ __launch_bounds__(NTH, 1) void gemm_bf16_dma_kernel(const GemmBatch b
     case gemm_kind(true, true, EPI_GELU): gemm_tile<true, true, EPI_GELU>(P, tm, tn, smem_raw, vec_c); break;
     case gemm_kind(true, false, EPI_DGELU): gemm_tile<true, false, EPI_DGELU>(P, tm, tn, smem_raw, vec_c); break;
     case gemm_kind(true, true, EPI_DGELU): gemm_tile<true, true, EPI_DGELU>(P, tm, tn, smem_raw, vec_c); break;
+    case gemm_kind(true, false, EPI_BF16): gemm_tile<true, false, EPI_BF16>(P, tm, tn, smem_raw, vec_c); break;
+    case gemm_kind(true, true, EPI_BF16): gemm_tile<true, true, EPI_BF16>(P, tm, tn, smem_raw, vec_c); break;
     default: break;  // layouts the library never issues with these epilogues
   }
 }
@@ -385,7 +387,7 @@ bool aligned(const void* p, int bytes) { return (reinterpret_cast<uintptr_t>(p) 
 // each operand's contiguous dimension, an extent along it that is a multiple
 // of 8 elements, operand byte ranges that the 32-bit buffer offsets can
 // address, and a (layout, epilogue) pair the kernel instantiates (the GELU
-// epilogues need a k-major A).
+// and bf16-output epilogues need a k-major A).
 bool gemm_bf16_dma_eligible(const GemmProb& p, bool a_kmajor, bool b_kmajor, int epi) {
   if (p.M <= 0 || p.N <= 0 || p.K <= 0 || p.K % 32 != 0) return false;
   if (epi != EPI_F32 && !a_kmajor) return false;

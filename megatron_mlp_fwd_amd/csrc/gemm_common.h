@@ -132,6 +132,14 @@ __device__ __forceinline__ void epilogue_store(const GemmProb& P, floatx4 v, int
           h[r] = __builtin_bit_cast(uint16_t, (__bf16)gv[r]);
         }
     }
+  } else if constexpr (EPI == EPI_BF16) {
+    uint16_t* c = static_cast<uint16_t*>(P.C) + off;
+    if (full) {
+      *reinterpret_cast<u32x2*>(c) = u32x2{pack_bf16(v[0], v[1]), pack_bf16(v[2], v[3])};
+    } else {
+      for (int r = 0; r < 4; ++r)
+        if (n + r < N) c[r] = __builtin_bit_cast(uint16_t, (__bf16)v[r]);
+    }
   } else {  // EPI_DGELU: C = acc * gelu'(P), gelu'(P) read from aux_in (may alias C)
     uint16_t* c = static_cast<uint16_t*>(P.C) + off;
     if (full) {

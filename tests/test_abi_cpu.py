@@ -102,3 +102,21 @@ def test_mlp_and_ce_reject_bad_arguments(lib):
     assert h(0, 1, 4, 8, p, p, p, p, N, N, 0, N) == binding.TPR_ERR_PARTITION
     assert h(2, 9, 4, 8, p, p, p, p, N, N, 0, N) == binding.TPR_ERR_DTYPE
     assert h(2, 1, 4, 8, p, p, p, p, N, N, 0, N) == binding.TPR_ERR_WORKSPACE
+
+
+def test_head_ce_workspace_and_bad_arguments(lib):
+    ws = lib.vocab_parallel_head_ce_workspace_bytes
+    # logits + dlogits (bf16), row losses, and 8 fp32 partials of dh
+    assert ws(8, 1, 4096, 4096, 128256) == 2 * 4096 * 128256 * 2 + 4096 * 4 + 8 * 4096 * 4096 * 4
+    assert ws(1, 0, 3, 5, 7) == 2 * 256 + 256                                    # fp32, one rank: no partials
+    assert ws(0, 1, 3, 5, 7) == 0                                               # invalid parts
+    f = lib.vocab_parallel_head_ce_fwd_bwd
+    p = ctypes.c_void_p(16)  # never dereferenced: validation stops first
+    assert f(2, 1, 0, -1, 4, 8, *[p] * 6, N, 0, N) == binding.TPR_ERR_SHAPE
+    assert f(2, 1, 0, 3, 4, 0, *[p] * 6, N, 0, N) == binding.TPR_ERR_SHAPE       # V = 0 with T > 0
+    assert f(0, 1, 0, 3, 4, 8, *[p] * 6, N, 0, N) == binding.TPR_ERR_PARTITION
+    assert f(2, 7, 0, 3, 4, 8, *[p] * 6, N, 0, N) == binding.TPR_ERR_DTYPE
+    assert f(2, 1, 5, 3, 4, 8, *[p] * 6, N, 0, N) == binding.TPR_ERR_DTYPE       # w_layout
+    assert f(2, 1, 0, 3, 4, 8, p, p, p, N, p, p, N, 0, N) == binding.TPR_ERR_NULLPTR
+    assert f(2, 1, 0, 3, 4, 8, *[p] * 6, N, 0, N) == binding.TPR_ERR_WORKSPACE
+    assert b"workspace" in lib.tprank_last_error()

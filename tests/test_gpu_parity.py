@@ -9,6 +9,8 @@ size.
 """
 import sys
 
+import math
+
 import numpy as np
 import pytest
 import torch
@@ -371,3 +373,50 @@ def test_determinism(tpr):
     r2 = tpr.tp_mlp_fwd_bwd(3, x, w1, w2, gy)
     for p, q in zip(r1, r2):
         assert torch.equal(p, q)
+
+
+# ---------------------------------------------------------------- vocab head + CE
+
+@pytest.mark.parametrize("layout", ["math", "torch"])
+@pytest.mark.parametrize("parts", [1, 3, 8])
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
+@pytest.mark.parametrize("T,d,V", [(37, 64, 1003), (256, 264, 4096), (5, 8, 3)])
+def test_head_ce(tpr, T, d, V, dtype, parts, layout):
+    say("vocab head + CE", T, d, V, dtype, parts, layout)
+    # Logits of standard deviation 2, like the CE workload: with bf16 logits
+    # the probabilities carry a relative error of about |z| 2^-9.
+    h, w, y = workloads.vocab_head(T, d, V, seed=T + d + V + parts, device=DEV, dtype=dtype,
+                                   w_std=2.0 / math.sqrt(d), w_layout=layout)
+    loss, dh, dw = tpr.vocab_parallel_head_ce_fwd_bwd(parts, h, w, y, w_layout=layout)
+    torch.cuda.synchronize()
+    wl, wdh, wdw = oracle.head_ce(f64(h), f64(w), y.cpu().numpy(), layout)
+    tol = tol_of(dtype)
+    assert abs(loss.item() - wl) <= tol * abs(wl)
+    assert rel_err(f64(dh), wdh) <= tol
+    assert rel_err(f64(dw), wdw) <= tol
+
+
+def test_head_ce_zero_rows(tpr):
+    say("vocab head + CE, T = 0")
+    h = torch.empty(0, 16, dtype=torch.bfloat16, device=DEV)
+    w = torch.randn(16, 40, device=DEV).to(torch.bfloat16)
+    y = torch.empty(0, dtype=torch.int64, device=DEV)
+    loss, dh, dw = tpr.vocab_parallel_head_ce_fwd_bwd(4, h, w, y)
+    torch.cuda.synchronize()
+    assert loss.item() == 0.0 and dh.shape == (0, 16)
+    assert torch.count_nonzero(dw).item() == 0
+
+
+def test_head_ce_llama3_8b_sized_sampled(tpr):
+    # Llama-3-8B hidden size with a 32000-entry vocabulary, 8 shards (the
+    # full 128256 vocabulary is the benchmark's; the fp64 oracle of a smaller
+    # vocabulary keeps the test in seconds), bf16.
+    say("vocab head + CE T=512 d=4096 V=32000 bf16, 8 shards")
+    T, d, V = 512, 4096, 32000
+    h, w, y = workloads.vocab_head(T, d, V, seed=3, device=DEV, w_std=2.0 / math.sqrt(d))
+    loss, dh, dw = tpr.vocab_parallel_head_ce_fwd_bwd(8, h, w, y)
+    torch.cuda.synchronize()
+    wl, wdh, wdw = oracle.head_ce(f64(h), f64(w), y.cpu().numpy())
+    assert abs(loss.item() - wl) <= TOL_BF16 * abs(wl)
+    assert rel_err(f64(dh), wdh) <= TOL_BF16
+    assert rel_err(f64(dw), wdw) <= TOL_BF16

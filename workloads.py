@@ -81,6 +81,16 @@ def inner_gemm(M, K, N, seed=0, device="cpu", dtype=torch.bfloat16, b_std=0.02):
     return a, b, gy
 
 
+def vocab_head(T, d, V, seed=0, device="cpu", dtype=torch.bfloat16, w_std=0.02, w_layout="math"):
+    """Hidden states h ~ N(0, 1) (T x d), a vocabulary head W ~ N(0, w_std)
+    (d x V, or V x d for the torch layout) and uniform labels."""
+    g = _gen(device, seed)
+    h = _normal((T, d), 1.0, g, device, dtype)
+    w = _normal((d, V) if w_layout == "math" else (V, d), w_std, g, device, dtype)
+    labels = torch.randint(0, V, (T,), generator=g, device=device, dtype=torch.int64)
+    return h, w, labels
+
+
 # The five workloads, by name and size.  ``kind`` says which entry point
 # consumes them.
 CONFIGS = {
@@ -90,4 +100,6 @@ CONFIGS = {
     "llama3_8b_tp8_rank_mlp": dict(kind="tp_mlp", tp=1, T=4096, d=4096, f=1792, w_layout="math", dtype="bf16"),
     "llama3_70b_tp8_rank_mlp": dict(kind="tp_mlp", tp=1, T=8192, d=8192, f=3584, w_layout="math", dtype="bf16"),
     "llama3_70b_tp8_inner_gemm": dict(kind="sharded_gemm", M=8192, K=1024, N=8192, parts=(1,), axis="inner", dtype="bf16"),
+    # next: the vocabulary-parallel output head in front of the CE (Llama-3-8B sizes)
+    "llama3_8b_vocab_head_ce_p8": dict(kind="vocab_head_ce", T=4096, d=4096, V=128256, parts=8, dtype="bf16"),
 }
