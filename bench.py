@@ -37,6 +37,7 @@ METRIC = "TP-rank MLP fwd+bwd TFLOP/s (% bf16 MFMA peak); vocab-CE HBM GB/s"
 MLP = dict(T=8192, d=8192, f=3584)
 INNER = dict(M=8192, K=1024, N=8192)
 CE = dict(T=4096, V=128256, parts=8)
+HEAD = dict(T=4096, d=4096, V=128256, parts=8)
 
 
 def kernel_source_digest():
@@ -131,12 +132,41 @@ def cpu_baseline(budget_s=10.0, max_reps=4):
                       f"{len(times)} runs of {dt:.2f} s on average, {os.cpu_count()} host CPUs visible"}
 
 
+def bench_head(tpr, workloads, dev, steps):
+    """The vocabulary-parallel output head + CE (Llama-3-8B hidden size and
+    vocabulary, 8 shards, bf16), timed on its own after the step: three GEMMs
+    of 2*T*d*V FLOP each plus the CE and the dh reduction per call."""
+    import torch
+
+    T, d, V, P = HEAD["T"], HEAD["d"], HEAD["V"], HEAD["parts"]
+    h, w, y = workloads.vocab_head(T, d, V, seed=5, device=dev, w_std=2.0 / d ** 0.5)
+    out = (torch.empty((), device=dev), torch.empty(T, d, device=dev), torch.empty(d, V, device=dev))
+    ws = torch.empty(tpr.vocab_parallel_head_ce_workspace_bytes(P, torch.bfloat16, T, d, V), dtype=torch.uint8,
+                     device=dev)
+    tpr.vocab_parallel_head_ce_fwd_bwd(P, h, w, y, out=out, workspace=ws)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(steps):
+        tpr.vocab_parallel_head_ce_fwd_bwd(P, h, w, y, out=out, workspace=ws)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    flop = 6.0 * T * d * V
+    tflops = flop / (ms * 1e-3) / 1e12
+    return {"config": dict(HEAD, dtype="bf16", w_layout="math"), "steps": steps, "ms": round(ms, 3),
+            "tflops": round(tflops, 1), "pct_of_bf16_peak": round(100.0 * tflops / PEAK_BF16_TFLOPS, 2),
+            "flop_per_call": flop}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--head-steps", type=int, default=3,
+                    help="timed calls of the vocabulary-parallel output head + CE (reported beside the step; 0 = skip)")
     ap.add_argument("--traffic-from", nargs=3, metavar=("FETCH_CSV", "WRITE_CSV", "COPY_BYTES"))
     ap.add_argument("--copy-bytes", type=int, default=0,
                     help="also run one plain copy kernel (torch.neg on fp32) of this many bytes before timing, "
@@ -224,6 +254,10 @@ def main():
     gemm_traffic = stored_traffic(GEMM_KERNEL + "_bytes_per_launch")
     ce_traffic = stored_traffic(CE_KERNEL + "_bytes_per_launch")
 
+    head = None
+    if args.head_steps > 0:
+        head = bench_head(tpr, workloads, dev, args.head_steps)
+
     line = {
         "metric": METRIC,
         "value": round(mlp_tflops, 2),
@@ -276,6 +310,8 @@ def main():
         },
         "kernel_source_digest": kernel_source_digest(),
     }
+    if head is not None:
+        line["vocab_head_ce"] = head
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline()
     print(json.dumps(line), flush=True)
