@@ -65,7 +65,7 @@ def stored_traffic(kernel):
 
 
 GEMM_KERNEL = "gemm_bf16_dma_kernel"
-CE_KERNEL = "ce_fast_kernel"
+CE_KERNEL = "ce_pair_kernel"
 COPY_KERNEL = "neg_kernel"
 
 
