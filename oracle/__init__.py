@@ -18,7 +18,10 @@ it cites:
   linears, the block-GEMM identity and the GELU MLP composed from them;
 * the multi-card tensor page's vocabulary-split output head (``head.py``):
   logits per vocabulary shard, the sharded cross-entropy, and the hidden
-  state's gradient summed across the shards.
+  state's gradient summed across the shards;
+* the same page's list of what a real cross-entropy must also handle
+  (``ce_options.py``): a padded vocabulary, ignored positions and label
+  smoothing, each checked against an unsharded full-vocabulary reference.
 
 Where a method reaches a result that has a plain definition (the unsharded
 product, the unsharded MLP, the unsharded cross-entropy), the oracle used for
@@ -35,6 +38,7 @@ from .matmul import AXES, check_matmul_args, matmul_grads, sharded_matmul, shard
 from .mlp import gelu, gelu_prime, to_math_layout, mlp_fwd_bwd, tp_mlp_fwd_bwd, mlp_sampled
 from .ce import cross_entropy, vocab_parallel_ce
 from .head import head_ce, vocab_parallel_head_ce
+from .ce_options import cross_entropy_opts, vocab_parallel_ce_opts
 
 __all__ = [
     "shard_range", "shard_ranges",
@@ -42,4 +46,5 @@ __all__ = [
     "gelu", "gelu_prime", "to_math_layout", "mlp_fwd_bwd", "tp_mlp_fwd_bwd", "mlp_sampled",
     "cross_entropy", "vocab_parallel_ce",
     "head_ce", "vocab_parallel_head_ce",
+    "cross_entropy_opts", "vocab_parallel_ce_opts",
 ]
