@@ -38,6 +38,8 @@ MLP = dict(T=8192, d=8192, f=3584)
 INNER = dict(M=8192, K=1024, N=8192)
 CE = dict(T=4096, V=128256, parts=8)
 HEAD = dict(T=4096, d=4096, V=128256, parts=8)
+MLP_8B = dict(T=4096, d=4096, f=1792)
+CE_OPTS = dict(T=4096, V=128256, v_valid=128000, parts=8, label_smoothing=0.1, ignore_frac=0.125)
 
 
 def kernel_source_digest():
@@ -159,6 +161,69 @@ def bench_head(tpr, workloads, dev, steps):
             "flop_per_call": flop}
 
 
+def bench_mlp_8b(tpr, workloads, dev, steps):
+    """The Llama-3-8B tensor-parallel-8 rank MLP fwd+bwd (T=4096, d=4096,
+    f=1792, bf16), timed on its own after the step and reported beside it."""
+    import torch
+
+    T, d, f = MLP_8B["T"], MLP_8B["d"], MLP_8B["f"]
+    x, w1, w2, gy = workloads.rank_mlp(T, d, f, seed=3, device=dev)
+    out = (torch.empty(T, d, device=dev), torch.empty(T, d, device=dev),
+           torch.empty(d, f, device=dev), torch.empty(f, d, device=dev))
+    ws = torch.empty(tpr.tp_mlp_workspace_bytes(1, torch.bfloat16, T, d, f), dtype=torch.uint8, device=dev)
+    for _ in range(2):
+        tpr.tp_mlp_fwd_bwd(1, x, w1, w2, gy, "math", out=out, workspace=ws)
+    torch.cuda.synchronize()
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(steps)]
+    for e in ev:
+        e[0].record()
+        tpr.tp_mlp_fwd_bwd(1, x, w1, w2, gy, "math", out=out, workspace=ws)
+        e[1].record()
+    torch.cuda.synchronize()
+    ms = sorted(e[0].elapsed_time(e[1]) for e in ev)
+    flop = 12.0 * T * d * f
+    mean = sum(ms) / len(ms)
+    tflops = flop / (mean * 1e-3) / 1e12
+    return {"config": dict(MLP_8B, dtype="bf16", w_layout="math"), "steps": steps, "ms": round(mean, 4),
+            "ms_median": round(ms[len(ms) // 2], 4), "ms_min": round(ms[0], 4), "tflops": round(tflops, 1),
+            "pct_of_bf16_peak": round(100.0 * tflops / PEAK_BF16_TFLOPS, 2), "flop_per_call": flop}
+
+
+def bench_ce_opts(tpr, workloads, dev, steps):
+    """The cross-entropy with options: a 128000-entry vocabulary padded to
+    128256 columns, 8 shards, label smoothing 0.1, about one position in
+    eight ignored.  Algorithmic bytes: 2 per vocabulary logit of a counted
+    row read, 2 per column of every row written."""
+    import torch
+
+    c = CE_OPTS
+    logits, labels = workloads.vocab_ce_opts(c["T"], c["V"], c["v_valid"], seed=6, device=dev,
+                                             ignore_frac=c["ignore_frac"])
+    out = (torch.empty((), device=dev), torch.empty_like(logits), None)
+    ws = torch.empty(tpr.vocab_parallel_ce_opts_workspace_bytes(c["parts"], c["T"], c["V"]), dtype=torch.uint8,
+                     device=dev)
+    call = lambda: tpr.vocab_parallel_ce_opts_fwd_bwd(c["parts"], logits, labels, v_valid=c["v_valid"],
+                                                      ignore_index=-100, label_smoothing=c["label_smoothing"],
+                                                      out=out, workspace=ws)
+    for _ in range(2):
+        call()
+    torch.cuda.synchronize()
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(steps)]
+    for e in ev:
+        e[0].record()
+        call()
+        e[1].record()
+    torch.cuda.synchronize()
+    ms = sorted(e[0].elapsed_time(e[1]) for e in ev)
+    n = int((labels != -100).sum().item())
+    nbytes = 2.0 * n * c["v_valid"] + 2.0 * c["T"] * c["V"]
+    mean = sum(ms) / len(ms)
+    gbs = nbytes / (mean * 1e-3) / 1e9
+    return {"config": dict(c, dtype="bf16", counted_rows=n), "steps": steps, "ms": round(mean, 4),
+            "ms_min": round(ms[0], 4), "gbs": round(gbs, 1), "pct_of_hbm_peak": round(100.0 * gbs / PEAK_HBM_GBS, 2),
+            "bytes_per_call": nbytes}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -167,6 +232,10 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--head-steps", type=int, default=3,
                     help="timed calls of the vocabulary-parallel output head + CE (reported beside the step; 0 = skip)")
+    ap.add_argument("--mlp-8b-steps", type=int, default=10,
+                    help="timed calls of the 8B-rank MLP fwd+bwd (reported beside the step; 0 = skip)")
+    ap.add_argument("--ce-opts-steps", type=int, default=10,
+                    help="timed calls of the cross-entropy with options (reported beside the step; 0 = skip)")
     ap.add_argument("--traffic-from", nargs=3, metavar=("FETCH_CSV", "WRITE_CSV", "COPY_BYTES"))
     ap.add_argument("--copy-bytes", type=int, default=0,
                     help="also run one plain copy kernel (torch.neg on fp32) of this many bytes before timing, "
@@ -257,6 +326,13 @@ def main():
     head = None
     if args.head_steps > 0:
         head = bench_head(tpr, workloads, dev, args.head_steps)
+    mlp_8b = None
+    if args.mlp_8b_steps > 0:
+        mlp_8b = bench_mlp_8b(tpr, workloads, dev, args.mlp_8b_steps)
+    ce_opts = None
+    if args.ce_opts_steps > 0:
+        ce_opts = bench_ce_opts(tpr, workloads, dev, args.ce_opts_steps)
+    med = lambda v: sorted(v)[len(v) // 2]
 
     line = {
         "metric": METRIC,
@@ -281,11 +357,16 @@ def main():
         },
         "mlp_pct_of_bf16_peak": round(100.0 * mlp_tflops / PEAK_BF16_TFLOPS, 2),
         "mlp_ms": round(avg(mlp_ms), 4),
+        "mlp_ms_median": round(med(mlp_ms), 4),
+        "mlp_ms_min": round(min(mlp_ms), 4),
         "inner_gemm_tflops": round(inner_tflops, 2),
         "inner_gemm_ms": round(avg(inner_ms), 4),
+        "inner_gemm_ms_min": round(min(inner_ms), 4),
         "vocab_ce_gbs": round(ce_gbs, 1),
         "vocab_ce_pct_of_hbm_peak": round(100.0 * ce_gbs / PEAK_HBM_GBS, 2),
         "vocab_ce_ms": round(avg(ce_ms), 4),
+        "vocab_ce_ms_median": round(med(ce_ms), 4),
+        "vocab_ce_ms_min": round(min(ce_ms), 4),
         "roofline": {
             "kernel": GEMM_KERNEL + " (4 grouped launches per step: 3 of the MLP call, 1 of the inner GEMM)",
             "bound": "mfma",
@@ -312,6 +393,10 @@ def main():
     }
     if head is not None:
         line["vocab_head_ce"] = head
+    if mlp_8b is not None:
+        line["mlp_8b_rank"] = mlp_8b
+    if ce_opts is not None:
+        line["vocab_ce_opts"] = ce_opts
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline()
     print(json.dumps(line), flush=True)

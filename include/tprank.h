@@ -51,6 +51,7 @@ extern "C" {
 #define TPR_ERR_WORKSPACE 4  /* ws_bytes smaller than the *_workspace_bytes() value */
 #define TPR_ERR_NULLPTR 5    /* a pointer that must be non-NULL is NULL */
 #define TPR_ERR_HIP 6        /* a HIP launch failed */
+#define TPR_ERR_VALUE 7      /* a scalar option outside its range */
 
 /* ---- enumerations ------------------------------------------------------ */
 #define TPR_ROWS 0     /* split M: A and G by rows        ([GEMM] 解题路线 step 2) */
@@ -172,6 +173,45 @@ int vocab_parallel_ce_fwd_bwd(int parts, int dtype, int64_t T, int64_t V,
                               const void* logits, const int64_t* labels,
                               float* loss, void* dlogits, float* shard_stats,
                               void* ws, size_t ws_bytes, void* stream);
+
+/* ---- cross-entropy options: padded vocabulary, ignore index, smoothing - */
+/*
+ * Bytes of workspace vocab_parallel_ce_opts_fwd_bwd() needs (the T per-row
+ * losses, fp32, and the counted-row total).  Returns 0 for invalid arguments.
+ */
+size_t vocab_parallel_ce_opts_workspace_bytes(int parts, int64_t T, int64_t V);
+
+/*
+ * [CARDS] 04 / VOCABULARY SHARDS, last paragraph: besides the plain loss a
+ * real implementation handles vocabulary padding, an ignore index and label
+ * smoothing, with the normalisation of an unsharded full-vocabulary
+ * reference.  Same shards and statistics as vocab_parallel_ce_fwd_bwd(),
+ * with these readings:
+ *   - columns j >= v_valid of each row (1 <= v_valid <= V) are padding: they
+ *     are not part of the softmax and their dlogits are 0;
+ *   - a row whose label equals ignore_index adds no loss and gets a zero
+ *     dlogits row; the mean is over the n counted rows (loss = NaN and all
+ *     dlogits 0 when n = 0, the mean over no rows); pass a value no label
+ *     takes (e.g. INT64_MIN) to count every row;
+ *   - label smoothing eps in [0, 1]: a counted row's target distribution is
+ *     q = (1 - eps) onehot(y) + eps / v_valid over the vocabulary columns,
+ *     L_i = -sum_j q_j log p_j = log s - (1 - eps)(z_y - m) - eps (mean_j z_j - m),
+ *     dlogits_ij = (p_ij - q_ij) / n.
+ *   logits: T x V in `dtype`;  labels: T int64, each ignore_index or in
+ *   [0, v_valid) (not checked on the device; another label gives an
+ *   unspecified loss but no out-of-bounds access);  loss: one fp32 on the
+ *   device;  dlogits: T x V in `dtype`;  shard_stats: NULL, or T x parts x 3
+ *   fp32 (m_r, s_r, t_r) over each shard's vocabulary columns (m_r = -inf,
+ *   s_r = 0 for a shard of padding only; t_r = 0 on ignored rows).
+ * T == 0 writes loss = NaN.
+ * Errors: SHAPE (also v_valid out of range), PARTITION, DTYPE, NULLPTR,
+ * WORKSPACE, VALUE (eps outside [0, 1]), HIP.
+ */
+int vocab_parallel_ce_opts_fwd_bwd(int parts, int dtype, int64_t T, int64_t V, int64_t v_valid,
+                                   int64_t ignore_index, float label_smoothing,
+                                   const void* logits, const int64_t* labels,
+                                   float* loss, void* dlogits, float* shard_stats,
+                                   void* ws, size_t ws_bytes, void* stream);
 
 /* ---- vocabulary-parallel output head with cross-entropy --------------- */
 /*

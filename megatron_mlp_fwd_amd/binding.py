@@ -15,7 +15,9 @@ import torch
 _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libtprank.so")
 
-TPR_OK, TPR_ERR_SHAPE, TPR_ERR_PARTITION, TPR_ERR_DTYPE, TPR_ERR_WORKSPACE, TPR_ERR_NULLPTR, TPR_ERR_HIP = range(7)
+(TPR_OK, TPR_ERR_SHAPE, TPR_ERR_PARTITION, TPR_ERR_DTYPE, TPR_ERR_WORKSPACE, TPR_ERR_NULLPTR, TPR_ERR_HIP,
+ TPR_ERR_VALUE) = range(8)
+NO_IGNORE = -(2 ** 63)  # an ignore_index no label takes: every row counts
 AXES = {"rows": 0, "columns": 1, "inner": 2}
 DTYPES = {torch.float32: 0, torch.bfloat16: 1}
 W_LAYOUTS = {"math": 0, "torch": 1}
@@ -31,6 +33,9 @@ _SIGS = {
     "tp_mlp_fwd_bwd": (_i32, [_i32, _i32, _i32, _i64, _i64, _i64, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
     "vocab_parallel_ce_workspace_bytes": (_sz, [_i32, _i64, _i64]),
     "vocab_parallel_ce_fwd_bwd": (_i32, [_i32, _i32, _i64, _i64, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
+    "vocab_parallel_ce_opts_workspace_bytes": (_sz, [_i32, _i64, _i64]),
+    "vocab_parallel_ce_opts_fwd_bwd": (_i32, [_i32, _i32, _i64, _i64, _i64, _i64, ctypes.c_float, _vp, _vp, _vp, _vp,
+                                              _vp, _vp, _sz, _vp]),
     "vocab_parallel_head_ce_workspace_bytes": (_sz, [_i32, _i32, _i64, _i64, _i64]),
     "vocab_parallel_head_ce_fwd_bwd": (_i32, [_i32, _i32, _i32, _i64, _i64, _i64, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
                                               _sz, _vp]),
@@ -216,6 +221,46 @@ def vocab_parallel_ce_fwd_bwd(parts, logits, labels, shard_stats=False, out=None
     with torch.cuda.device(dev):
         _check(lib.vocab_parallel_ce_fwd_bwd(parts, DTYPES[dt], T, V, _ptr(logits), _ptr(labels), loss.data_ptr(),
                                              _ptr(dlogits), _ptr(stats), _ptr(ws), wsb, _stream(stream)))
+    return loss, dlogits, stats
+
+
+def vocab_parallel_ce_opts_workspace_bytes(parts, T, V):
+    return load_library().vocab_parallel_ce_opts_workspace_bytes(parts, T, V)
+
+
+def vocab_parallel_ce_opts_fwd_bwd(parts, logits, labels, v_valid=None, ignore_index=-100, label_smoothing=0.0,
+                                   shard_stats=False, out=None, workspace=None, stream=None):
+    """Cross-entropy with options over the rows of ``logits`` (T x V, the
+    vocabulary split into ``parts`` shards): columns from ``v_valid`` on are
+    padding, rows labelled ``ignore_index`` (None: no row is ignored) are left
+    out of the mean, and ``label_smoothing`` spreads that share of the target
+    over the vocabulary.  Returns (loss, dlogits, stats or None) like
+    vocab_parallel_ce_fwd_bwd."""
+    lib = load_library()
+    dt = logits.dtype
+    if dt not in DTYPES:
+        raise ValueError(f"unsupported dtype {dt}")
+    if logits.dim() != 2:
+        raise ValueError("logits must be 2-D")
+    T, V = logits.shape
+    vv = V if v_valid is None else int(v_valid)
+    ign = NO_IGNORE if ignore_index is None else int(ignore_index)
+    dev = logits.device
+    _need(logits, "logits", (T, V), dt, dev)
+    _need(labels, "labels", (T,), torch.int64, dev)
+    if out is None:
+        out = (torch.empty((), device=dev), torch.empty(T, V, dtype=dt, device=dev),
+               torch.empty(T, parts, 3, device=dev) if shard_stats else None)
+    loss, dlogits, stats = out
+    _need(loss, "loss", (), torch.float32, dev)
+    _need(dlogits, "dlogits", (T, V), dt, dev)
+    if stats is not None:
+        _need(stats, "shard_stats", (T, parts, 3), torch.float32, dev)
+    ws, wsb = _workspace(lib.vocab_parallel_ce_opts_workspace_bytes(parts, T, V), dev, workspace)
+    with torch.cuda.device(dev):
+        _check(lib.vocab_parallel_ce_opts_fwd_bwd(parts, DTYPES[dt], T, V, vv, ign, float(label_smoothing),
+                                                  _ptr(logits), _ptr(labels), loss.data_ptr(), _ptr(dlogits),
+                                                  _ptr(stats), _ptr(ws), wsb, _stream(stream)))
     return loss, dlogits, stats
 
 

@@ -341,6 +341,52 @@ int vocab_parallel_ce_fwd_bwd(int parts, int dtype, int64_t T, int64_t V, const 
   return TPR_OK;
 }
 
+// ---------------------------------------------------------------- CE options
+size_t vocab_parallel_ce_opts_workspace_bytes(int parts, int64_t T, int64_t V) {
+  if (parts < 1 || T < 0 || V < 0) return 0;
+  return align256((size_t)T * 4) + 256;  // per-row losses, then the counted-row total and its reciprocal
+}
+
+int vocab_parallel_ce_opts_fwd_bwd(int parts, int dtype, int64_t T, int64_t V, int64_t v_valid, int64_t ignore_index,
+                                   float label_smoothing, const void* logits, const int64_t* labels, float* loss,
+                                   void* dlogits, float* shard_stats, void* ws, size_t ws_bytes, void* stream) {
+  if (T < 0 || V < 0 || T > UINT_MAX || V / 8 > INT_MAX)
+    return fail(TPR_ERR_SHAPE, "T and V out of range (got %lld, %lld)", (long long)T, (long long)V);
+  if (T > 0 && V == 0) return fail(TPR_ERR_SHAPE, "V must be >= 1 when T > 0");
+  if (v_valid < (V > 0 ? 1 : 0) || v_valid > V)
+    return fail(TPR_ERR_SHAPE, "v_valid must be in [1, V] (got %lld, V = %lld)", (long long)v_valid, (long long)V);
+  if (parts < 1) return fail(TPR_ERR_PARTITION, "parts must be >= 1 (got %d)", parts);
+  if (!dtype_ok(dtype)) return fail(TPR_ERR_DTYPE, "unknown dtype %d", dtype);
+  if (!(label_smoothing >= 0.f && label_smoothing <= 1.f))
+    return fail(TPR_ERR_VALUE, "label_smoothing must be in [0, 1] (got %g)", (double)label_smoothing);
+  if (loss == nullptr || (T > 0 && (logits == nullptr || labels == nullptr || dlogits == nullptr)))
+    return fail(TPR_ERR_NULLPTR, "loss, logits, labels or dlogits is NULL");
+  const size_t need = vocab_parallel_ce_opts_workspace_bytes(parts, T, V);
+  if (ws_bytes < need || ws == nullptr)
+    return fail(TPR_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", need, ws_bytes);
+  char* wsb = static_cast<char*>(ws);
+  tpr::CeArgs a{};
+  a.logits = logits;
+  a.labels = labels;
+  a.dlogits = dlogits;
+  a.shard_stats = shard_stats;
+  a.row_loss = reinterpret_cast<float*>(wsb);
+  a.loss = loss;
+  a.T = T;
+  a.V = V;
+  a.parts = parts;
+  a.dtype = dtype;
+  a.opt = true;
+  a.v_valid = v_valid;
+  a.ignore_index = ignore_index;
+  a.smoothing = label_smoothing;
+  a.count = reinterpret_cast<int*>(wsb + align256((size_t)T * 4));
+  a.inv_count = reinterpret_cast<float*>(wsb + align256((size_t)T * 4) + 4);
+  const hipError_t he = tpr::launch_vocab_ce(a, static_cast<hipStream_t>(stream));
+  if (he != hipSuccess) return hip_fail(he, "vocab CE launch");
+  return TPR_OK;
+}
+
 // ---------------------------------------------------------------- vocab head + CE
 size_t vocab_parallel_head_ce_workspace_bytes(int parts, int dtype, int64_t T, int64_t d, int64_t V) {
   if (parts < 1 || !dtype_ok(dtype) || T < 0 || d < 0 || V < 0) return 0;

@@ -75,6 +75,15 @@ struct CeArgs {
   int64_t T, V;
   int parts;
   int dtype;  // TPR_F32 / TPR_BF16
+  // Options (used when `opt` is set): columns >= v_valid are vocabulary
+  // padding; rows whose label equals ignore_index add no loss and get a zero
+  // gradient, and the mean is over the counted rows; label smoothing eps.
+  bool opt;
+  int64_t v_valid;
+  int64_t ignore_index;
+  float smoothing;
+  int* count;        // workspace: counted rows (opt)
+  float* inv_count;  // workspace: 1 / counted rows, 0 if none (opt)
 };
 hipError_t launch_vocab_ce(const CeArgs& a, hipStream_t s);
 

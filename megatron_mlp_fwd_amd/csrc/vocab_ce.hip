@@ -25,6 +25,11 @@
 // workgroup per row, three passes over the row (max per shard, sum and
 // target per shard, gradient).  Same arithmetic, the logits are re-read.
 //
+// Options (a padded vocabulary, ignored rows, label smoothing; the same
+// page's list of what a real cross-entropy must also handle) run in the
+// paired kernel's CE_OPT / CE_OPT_SMOOTH instances or the general path, after
+// a one-workgroup kernel that counts the rows that take part in the mean.
+//
 // A final single-workgroup kernel averages the per-row losses in a fixed
 // order (fp64 accumulation).
 #include "common.h"
@@ -258,6 +263,21 @@ __global__ __launch_bounds__(CE_NT, 1) void ce_fast_kernel(const uint16_t* __res
 }
 
 
+// ---------------------------------------------------------------- options
+// Padded vocabulary, ignored rows, label smoothing (see CeArgs).  For a
+// counted row with n counted rows in all, v_valid vocabulary columns and
+// smoothing eps, the target distribution is q = (1 - eps) onehot(y) +
+// eps / v_valid, the row loss is log s - (1 - eps)(z_y - m) - eps (mean z - m)
+// over the vocabulary columns, and dL/dz_j = (p_j - q_j) / n; padding columns
+// and ignored rows get zero gradient.
+struct CeOpt {
+  int64_t vv;            // vocabulary columns per row (<= V)
+  int64_t ignore;        // label of ignored rows
+  float eps;             // label smoothing
+  const float* inv_cnt;  // 1 / counted rows, written by ce_count_kernel
+};
+enum { CE_PLAIN = 0, CE_OPT = 1, CE_OPT_SMOOTH = 2 };
+
 // ---------------------------------------------------------------- paired path
 // Rows without per-shard statistics, bf16: two 512-thread workgroups per CU,
 // each holding its whole row: CP_RS 16-byte slots per thread in registers
@@ -271,22 +291,43 @@ constexpr int CP_RS = 22;           // register slots per thread
 constexpr int CP_LDS_VEC = 4864;    // LDS capacity in 16-byte vectors (76 KB)
 constexpr uint32_t CP_OOB = 0x80000000u;
 
-__global__ __launch_bounds__(CP_NT) __attribute__((amdgpu_waves_per_eu(4, 4))) void ce_pair_kernel(const uint16_t* __restrict__ logits,
-                                                            const int64_t* __restrict__ labels,
-                                                            uint16_t* __restrict__ dlogits, float* __restrict__ row_loss,
-                                                            int64_t V, float invT) {
+template <int MODE>
+__global__ __launch_bounds__(CP_NT) __attribute__((amdgpu_waves_per_eu(4, 4))) void ce_pair_kernel(
+    const uint16_t* __restrict__ logits, const int64_t* __restrict__ labels, uint16_t* __restrict__ dlogits,
+    float* __restrict__ row_loss, int64_t V, float invT, CeOpt o) {
+  constexpr bool OPT = MODE != CE_PLAIN, SMOOTH = MODE == CE_OPT_SMOOTH;
   __shared__ __attribute__((aligned(1024))) u32x4 part[CP_LDS_VEC];
   __shared__ float red[CP_NW];
+  __shared__ float red_z[CP_NW];
+  __shared__ float tail_sh[8];  // the vocabulary's last rem logits, then their exp
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
   const int64_t row = blockIdx.x;
   const int nvec = (int)(V / 8);
-  const int nreg = nvec < CP_RS * CP_NT ? nvec : CP_RS * CP_NT;  // vectors held in registers
-  const int nlds = nvec - nreg;                                  // vectors held in LDS
+  // With options, whole vocabulary vectors go through the slots; the
+  // vocabulary's last rem (< 8) columns are one element each on lanes 0..rem-1
+  // of wave 0, and the padding vectors after them are only zero-filled.
+  const int nfull = OPT ? (int)(o.vv >> 3) : nvec;
+  const int rem = OPT ? (int)(o.vv & 7) : 0;
+  const int nreg = nfull < CP_RS * CP_NT ? nfull : CP_RS * CP_NT;  // vectors held in registers
+  const int nlds = nfull - nreg;                                    // vectors held in LDS
   const __amdgpu_buffer_rsrc_t rz =
       __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(logits + row * V), (short)0, (int)(V * 2), 0x00020000);
   const __amdgpu_buffer_rsrc_t rd =
       __builtin_amdgcn_make_buffer_rsrc(dlogits + row * V, (short)0, (int)(V * 2), 0x00020000);
   const int64_t y = labels[row];
+  const u32x4 zero{0u, 0u, 0u, 0u};
+  if constexpr (OPT) {
+    if (y == o.ignore) {  // ignored row (uniform over the workgroup): zero gradient, no loss
+      for (int i = tid; i < nvec; i += CP_NT)
+        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(__attribute__((ext_vector_type(4))) int, zero),
+                                               rd, (uint32_t)(16 * i), 0, 2);
+      if (tid == 0) row_loss[row] = 0.f;
+      return;
+    }
+  }
+  const float inv = OPT ? *o.inv_cnt : invT;
+  const bool tail = OPT && wid == 0 && lane < rem;
+  if (tail) tail_sh[lane] = __uint_as_float((uint32_t)logits[row * V + 8 * nfull + lane] << 16);
 
   // LDS part: wave instruction j moves vectors nreg + 64 j .. + 63 (lanes past
   // the row end read zeros and are never used).
@@ -306,7 +347,7 @@ __global__ __launch_bounds__(CP_NT) __attribute__((amdgpu_waves_per_eu(4, 4))) v
   __syncthreads();
 
   // Row maximum.
-  float run = -INFINITY;
+  float run = tail ? tail_sh[lane] : -INFINITY;
 #pragma unroll
   for (int s = 0; s < CP_RS; ++s)
     if (s * CP_NT + tid < nreg) run = fmaxf(run, vec_max(v[s]));
@@ -328,13 +369,23 @@ __global__ __launch_bounds__(CP_NT) __attribute__((amdgpu_waves_per_eu(4, 4))) v
   asm volatile("" : "+v"(t2));
 
   // exp(z - m) once per logit, summed in fp32 and kept as fp16 in place.
-  const bool y_ok = y >= 0 && y < V;
+  const int vlim = OPT ? (int)o.vv : nvec * 8;
+  const bool y_ok = y >= 0 && y < vlim;
   const float zy = y_ok ? __uint_as_float((uint32_t)logits[row * V + (y_ok ? y : 0)] << 16) : 0.f;
-  float sum = 0.f;
+  // (with smoothing, the same pass sums the vocabulary logits)
+  float sum = 0.f, zs = 0.f;
+  if (tail) {
+    const float zt = tail_sh[lane];
+    sum = __builtin_amdgcn_exp2f(zt * LOG2E - mL);
+    zs = zt;
+    tail_sh[lane] = sum;  // the same lane reads it back for the gradient
+  }
   auto expv = [&](u32x4& x) {
     float ex[8];
 #pragma unroll
     for (int e = 0; e < 8; ++e) ex[e] = __builtin_amdgcn_exp2f(elem(x, e) * LOG2E - mL);
+    if constexpr (SMOOTH)
+      zs += ((elem(x, 0) + elem(x, 1)) + (elem(x, 2) + elem(x, 3))) + ((elem(x, 4) + elem(x, 5)) + (elem(x, 6) + elem(x, 7)));
     sum += ((ex[0] + ex[1]) + (ex[2] + ex[3])) + ((ex[4] + ex[5]) + (ex[6] + ex[7]));
 #pragma unroll
     for (int q = 0; q < 4; ++q) x[q] = pack_f16(ex[2 * q], ex[2 * q + 1]);
@@ -354,20 +405,32 @@ __global__ __launch_bounds__(CP_NT) __attribute__((amdgpu_waves_per_eu(4, 4))) v
   {
     const float w = wave_sum(sum);
     if (lane == 0) red[wid] = w;
+    if constexpr (SMOOTH) {
+      const float wz = wave_sum(zs);
+      if (lane == 0) red_z[wid] = wz;
+    }
   }
   __syncthreads();
   float ssum = red[0];
   for (int w = 1; w < CP_NW; ++w) ssum += red[w];
-  if (tid == 0) row_loss[row] = logf(ssum) - (y_ok ? zy - m : 0.f);
+  float zsum = 0.f;
+  if constexpr (SMOOTH)
+    for (int w = 0; w < CP_NW; ++w) zsum += red_z[w];
+  const float eps = SMOOTH ? o.eps : 0.f;
+  if (tid == 0)
+    row_loss[row] =
+        logf(ssum) - (1.f - eps) * (y_ok ? zy - m : 0.f) - (SMOOTH ? eps * (zsum / (float)vlim - m) : 0.f);
 
   // Gradient, written once; the lane that wrote the vector holding the
   // target rewrites that element afterwards (program order).
-  const float scale = invT / ssum;
+  const float scale = inv / ssum;
+  const float c = SMOOTH ? eps * inv / (float)vlim : 0.f;  // smoothing share of each vocabulary column
+  const float cy = (1.f - eps) * inv;                       // the target's share
   const int vy = y_ok ? (int)(y >> 3) : -1;
   auto grad = [&](const u32x4& x, int i) {
     float g[8];
 #pragma unroll
-    for (int e = 0; e < 8; ++e) g[e] = f16_elem(x, e) * scale;
+    for (int e = 0; e < 8; ++e) g[e] = SMOOTH ? f16_elem(x, e) * scale - c : f16_elem(x, e) * scale;
     const u32x4 w{pack_bf16(g[0], g[1]), pack_bf16(g[2], g[3]), pack_bf16(g[4], g[5]), pack_bf16(g[6], g[7])};
     __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(__attribute__((ext_vector_type(4))) int, w), rd,
                                            (uint32_t)(16 * i), 0, 2);
@@ -387,8 +450,20 @@ __global__ __launch_bounds__(CP_NT) __attribute__((amdgpu_waves_per_eu(4, 4))) v
     grad(part[j], nreg + j);
   }
   if (owner) {
-    const float gy = __builtin_amdgcn_exp2f(zy * LOG2E - mL) * scale - invT;
+    const float gy = __builtin_amdgcn_exp2f(zy * LOG2E - mL) * scale - c - cy;
     dlogits[row * V + y] = __builtin_bit_cast(uint16_t, (__bf16)gy);
+  }
+  if constexpr (OPT) {
+    // The partial last vector (vocabulary lanes, then padding) and the
+    // padding vectors after it.
+    if (rem > 0 && wid == 0 && lane < 8) {
+      const int col = 8 * nfull + lane;
+      const float g = lane < rem ? tail_sh[lane] * scale - c - (col == y ? cy : 0.f) : 0.f;
+      dlogits[row * V + col] = __builtin_bit_cast(uint16_t, (__bf16)g);
+    }
+    for (int i = nfull + (rem > 0 ? 1 : 0) + tid; i < nvec; i += CP_NT)
+      __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(__attribute__((ext_vector_type(4))) int, zero), rd,
+                                             (uint32_t)(16 * i), 0, 2);
   }
 }
 
@@ -427,7 +502,7 @@ template <typename T>
 __global__ __launch_bounds__(256) void ce_general_kernel(const T* __restrict__ logits,
                                                          const int64_t* __restrict__ labels, T* __restrict__ dlogits,
                                                          float* __restrict__ row_loss, float* __restrict__ stats,
-                                                         int64_t V, int P, float invT) {
+                                                         int64_t V, int P, float invT, bool opt, CeOpt o) {
   __shared__ float scratch[4];
   const int tid = threadIdx.x;
   const int64_t row = blockIdx.x;
@@ -435,10 +510,15 @@ __global__ __launch_bounds__(256) void ce_general_kernel(const T* __restrict__ l
   T* __restrict__ dz = dlogits + row * V;
   const int64_t y = labels[row];
   const int64_t base = V / P, extra = V % P;
+  const int64_t vv = opt ? o.vv : V;         // columns past vv are padding
+  const bool counted = !opt || y != o.ignore;
+  const float eps = opt ? o.eps : 0.f;
+  const float inv = opt ? *o.inv_cnt : invT;
 
   float m = -INFINITY;
   for (int r = 0; r < P; ++r) {
-    const int64_t lo = r * base + (r < extra ? r : extra), hi = lo + base + (r < extra ? 1 : 0);
+    const int64_t lo = r * base + (r < extra ? r : extra), hi0 = lo + base + (r < extra ? 1 : 0);
+    const int64_t hi = hi0 < vv ? hi0 : vv;
     float loc = -INFINITY;
     for (int64_t j = lo + tid; j < hi; j += 256) loc = fmaxf(loc, ld_logit(z, j));
     const float mr = block_reduce<true>(loc, scratch);
@@ -446,13 +526,18 @@ __global__ __launch_bounds__(256) void ce_general_kernel(const T* __restrict__ l
     if (stats != nullptr && tid == 0) stats[(row * P + r) * 3 + 0] = mr;
   }
   const float mL = m * LOG2E;
-  float ssum = 0.f, tsum = 0.f;
+  float ssum = 0.f, tsum = 0.f, zloc = 0.f;
   for (int r = 0; r < P; ++r) {
-    const int64_t lo = r * base + (r < extra ? r : extra), hi = lo + base + (r < extra ? 1 : 0);
+    const int64_t lo = r * base + (r < extra ? r : extra), hi0 = lo + base + (r < extra ? 1 : 0);
+    const int64_t hi = hi0 < vv ? hi0 : vv;
     float loc = 0.f;
-    for (int64_t j = lo + tid; j < hi; j += 256) loc += __builtin_amdgcn_exp2f(ld_logit(z, j) * LOG2E - mL);
+    for (int64_t j = lo + tid; j < hi; j += 256) {
+      const float zj = ld_logit(z, j);
+      loc += __builtin_amdgcn_exp2f(zj * LOG2E - mL);
+      zloc += zj;
+    }
     const float sr = block_reduce<false>(loc, scratch);
-    const float tr = (y >= lo && y < hi) ? ld_logit(z, y) - m : 0.f;
+    const float tr = (counted && y >= lo && y < hi) ? ld_logit(z, y) - m : 0.f;
     ssum += sr;
     tsum += tr;
     if (stats != nullptr && tid == 0) {
@@ -460,17 +545,46 @@ __global__ __launch_bounds__(256) void ce_general_kernel(const T* __restrict__ l
       stats[(row * P + r) * 3 + 2] = tr;
     }
   }
-  if (tid == 0) row_loss[row] = logf(ssum) - tsum;
-  const float scale = invT / ssum;
+  const float zsum = eps != 0.f ? block_reduce<false>(zloc, scratch) : 0.f;
+  if (tid == 0)
+    row_loss[row] = counted ? logf(ssum) - (1.f - eps) * tsum - eps * (zsum / (float)vv - m) : 0.f;
+  const float scale = counted ? inv / ssum : 0.f;
+  const float c = counted ? eps * inv / (float)vv : 0.f;
+  const float cy = counted ? (1.f - eps) * inv : 0.f;
   for (int64_t j = tid; j < V; j += 256) {
-    float g = __builtin_amdgcn_exp2f(ld_logit(z, j) * LOG2E - mL) * scale;
-    if (j == y) g -= invT;
+    float g = 0.f;
+    if (j < vv && counted) {
+      g = __builtin_amdgcn_exp2f(ld_logit(z, j) * LOG2E - mL) * scale - c;
+      if (j == y) g -= cy;
+    }
     st_grad(dz, j, g);
   }
 }
 
+// Counted rows (label != ignore_index) and their reciprocal, for the options.
+__global__ __launch_bounds__(1024) void ce_count_kernel(const int64_t* __restrict__ labels, int64_t T,
+                                                        int64_t ignore, int* __restrict__ count,
+                                                        float* __restrict__ inv_count) {
+  __shared__ int part[16];
+  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+  int c = 0;
+  for (int64_t i = tid; i < T; i += 1024) c += labels[i] != ignore ? 1 : 0;
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) c += __shfl_xor(c, off, 64);
+  if (lane == 0) part[wid] = c;
+  __syncthreads();
+  if (tid == 0) {
+    int n = 0;
+    for (int w = 0; w < 16; ++w) n += part[w];
+    count[0] = n;
+    inv_count[0] = n > 0 ? (float)(1.0 / (double)n) : 0.f;
+  }
+}
+
+// Mean of the per-row losses over T rows, or over *count rows when count is
+// given (NaN when that is 0: a mean over no rows).
 __global__ __launch_bounds__(1024) void loss_mean_kernel(const float* __restrict__ row_loss, int64_t T,
-                                                         float* __restrict__ loss) {
+                                                         const int* __restrict__ count, float* __restrict__ loss) {
   __shared__ double part[16];
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
   double acc = 0.0;
@@ -482,7 +596,12 @@ __global__ __launch_bounds__(1024) void loss_mean_kernel(const float* __restrict
   if (tid == 0) {
     double s = 0.0;
     for (int w = 0; w < 16; ++w) s += part[w];
-    loss[0] = T > 0 ? (float)(s / (double)T) : 0.f;
+    if (count != nullptr) {
+      const int n = T > 0 ? count[0] : 0;
+      loss[0] = n > 0 ? (float)(s / (double)n) : __builtin_nanf("");
+    } else {
+      loss[0] = T > 0 ? (float)(s / (double)T) : 0.f;
+    }
   }
 }
 
@@ -491,11 +610,24 @@ bool aligned16(const void* p) { return reinterpret_cast<uintptr_t>(p) % 16 == 0;
 }  // namespace
 
 hipError_t launch_vocab_ce(const CeArgs& a, hipStream_t s) {
+  CeOpt o{};
+  o.vv = a.opt ? a.v_valid : a.V;
+  o.ignore = a.ignore_index;
+  o.eps = a.opt ? a.smoothing : 0.f;
+  o.inv_cnt = a.inv_count;
   if (a.T > 0) {
     const float invT = (float)(1.0 / (double)a.T);
+    if (a.opt) {
+      hipLaunchKernelGGL(ce_count_kernel, dim3(1), dim3(1024), 0, s, a.labels, a.T, a.ignore_index, a.count,
+                         a.inv_count);
+      const hipError_t e = hipGetLastError();
+      if (e != hipSuccess) return e;
+    }
     const int64_t base = a.V / a.parts, extra = a.V % a.parts;
-    // Fast path eligibility and slot table.
-    bool fast = a.dtype == 1 && a.V % 8 == 0 && a.parts <= CE_PMAX && aligned16(a.logits) && aligned16(a.dlogits);
+    // Fast path eligibility and slot table (rows with per-shard statistics
+    // and no options).
+    bool fast = !a.opt && a.dtype == 1 && a.V % 8 == 0 && a.parts <= CE_PMAX && aligned16(a.logits) &&
+                aligned16(a.dlogits);
     CeSlots S{};
     S.P = a.parts;
     if (fast) {
@@ -526,32 +658,38 @@ hipError_t launch_vocab_ce(const CeArgs& a, hipStream_t s) {
     const int64_t nvec = a.V / 8, nlds = nvec - (nvec < CP_RS * CP_NT ? nvec : CP_RS * CP_NT);
     const bool pair = a.dtype == 1 && a.shard_stats == nullptr && a.V % 8 == 0 && aligned16(a.logits) &&
                       aligned16(a.dlogits) && (nlds + 63) / 64 * 64 <= CP_LDS_VEC;
+    const uint16_t* zb = static_cast<const uint16_t*>(a.logits);
+    uint16_t* db = static_cast<uint16_t*>(a.dlogits);
     if (pair) {
-      hipLaunchKernelGGL(ce_pair_kernel, dim3((unsigned)a.T), dim3(CP_NT), 0, s,
-                         static_cast<const uint16_t*>(a.logits), a.labels, static_cast<uint16_t*>(a.dlogits),
-                         a.row_loss, a.V, invT);
+      if (!a.opt)
+        hipLaunchKernelGGL(ce_pair_kernel<CE_PLAIN>, dim3((unsigned)a.T), dim3(CP_NT), 0, s, zb, a.labels, db,
+                           a.row_loss, a.V, invT, o);
+      else if (a.smoothing == 0.f)
+        hipLaunchKernelGGL(ce_pair_kernel<CE_OPT>, dim3((unsigned)a.T), dim3(CP_NT), 0, s, zb, a.labels, db,
+                           a.row_loss, a.V, invT, o);
+      else
+        hipLaunchKernelGGL(ce_pair_kernel<CE_OPT_SMOOTH>, dim3((unsigned)a.T), dim3(CP_NT), 0, s, zb, a.labels, db,
+                           a.row_loss, a.V, invT, o);
     } else if (fast) {
       if (a.shard_stats != nullptr)
-        hipLaunchKernelGGL(ce_fast_kernel<true>, dim3((unsigned)a.T), dim3(CE_NT), 0, s,
-                           static_cast<const uint16_t*>(a.logits), a.labels, static_cast<uint16_t*>(a.dlogits),
+        hipLaunchKernelGGL(ce_fast_kernel<true>, dim3((unsigned)a.T), dim3(CE_NT), 0, s, zb, a.labels, db,
                            a.row_loss, a.shard_stats, a.V, invT, S);
       else
-        hipLaunchKernelGGL(ce_fast_kernel<false>, dim3((unsigned)a.T), dim3(CE_NT), 0, s,
-                           static_cast<const uint16_t*>(a.logits), a.labels, static_cast<uint16_t*>(a.dlogits),
+        hipLaunchKernelGGL(ce_fast_kernel<false>, dim3((unsigned)a.T), dim3(CE_NT), 0, s, zb, a.labels, db,
                            a.row_loss, nullptr, a.V, invT, S);
     } else if (a.dtype == 1) {
-      hipLaunchKernelGGL(ce_general_kernel<uint16_t>, dim3((unsigned)a.T), dim3(256), 0, s,
-                         static_cast<const uint16_t*>(a.logits), a.labels, static_cast<uint16_t*>(a.dlogits),
-                         a.row_loss, a.shard_stats, a.V, a.parts, invT);
+      hipLaunchKernelGGL(ce_general_kernel<uint16_t>, dim3((unsigned)a.T), dim3(256), 0, s, zb, a.labels, db,
+                         a.row_loss, a.shard_stats, a.V, a.parts, invT, a.opt, o);
     } else {
       hipLaunchKernelGGL(ce_general_kernel<float>, dim3((unsigned)a.T), dim3(256), 0, s,
                          static_cast<const float*>(a.logits), a.labels, static_cast<float*>(a.dlogits), a.row_loss,
-                         a.shard_stats, a.V, a.parts, invT);
+                         a.shard_stats, a.V, a.parts, invT, a.opt, o);
     }
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
-  hipLaunchKernelGGL(loss_mean_kernel, dim3(1), dim3(1024), 0, s, a.row_loss, a.T, a.loss);
+  hipLaunchKernelGGL(loss_mean_kernel, dim3(1), dim3(1024), 0, s, a.row_loss, a.T,
+                     a.opt ? static_cast<const int*>(a.count) : nullptr, a.loss);
   return hipGetLastError();
 }
 

@@ -120,3 +120,25 @@ def test_head_ce_workspace_and_bad_arguments(lib):
     assert f(2, 1, 0, 3, 4, 8, p, p, p, N, p, p, N, 0, N) == binding.TPR_ERR_NULLPTR
     assert f(2, 1, 0, 3, 4, 8, *[p] * 6, N, 0, N) == binding.TPR_ERR_WORKSPACE
     assert b"workspace" in lib.tprank_last_error()
+
+
+def test_ce_opts_workspace_and_bad_arguments(lib):
+    ws = lib.vocab_parallel_ce_opts_workspace_bytes
+    assert ws(8, 4096, 128256) == 4096 * 4 + 256   # row losses, then the counted-row total
+    assert ws(1, 3, 5) == 256 + 256
+    assert ws(0, 3, 5) == 0
+    f = lib.vocab_parallel_ce_opts_fwd_bwd
+    p = ctypes.c_void_p(16)  # never dereferenced: validation stops first
+    ign = binding.NO_IGNORE
+    assert f(2, 1, -1, 8, 8, ign, 0.0, p, p, p, p, N, p, 4096, N) == binding.TPR_ERR_SHAPE
+    assert f(2, 1, 3, 8, 9, ign, 0.0, p, p, p, p, N, p, 4096, N) == binding.TPR_ERR_SHAPE      # v_valid > V
+    assert f(2, 1, 3, 8, 0, ign, 0.0, p, p, p, p, N, p, 4096, N) == binding.TPR_ERR_SHAPE      # v_valid < 1
+    assert f(0, 1, 3, 8, 8, ign, 0.0, p, p, p, p, N, p, 4096, N) == binding.TPR_ERR_PARTITION
+    assert f(2, 9, 3, 8, 8, ign, 0.0, p, p, p, p, N, p, 4096, N) == binding.TPR_ERR_DTYPE
+    assert f(2, 1, 3, 8, 8, ign, 1.5, p, p, p, p, N, p, 4096, N) == binding.TPR_ERR_VALUE
+    assert f(2, 1, 3, 8, 8, ign, -0.1, p, p, p, p, N, p, 4096, N) == binding.TPR_ERR_VALUE
+    assert f(2, 1, 3, 8, 8, ign, float("nan"), p, p, p, p, N, p, 4096, N) == binding.TPR_ERR_VALUE
+    assert b"label_smoothing" in lib.tprank_last_error()
+    assert f(2, 1, 3, 8, 8, ign, 0.1, p, N, p, p, N, p, 4096, N) == binding.TPR_ERR_NULLPTR
+    assert f(2, 1, 3, 8, 8, ign, 0.1, p, p, p, p, N, p, 16, N) == binding.TPR_ERR_WORKSPACE
+    assert f(2, 1, 3, 8, 8, ign, 0.1, p, p, p, p, N, N, 4096, N) == binding.TPR_ERR_WORKSPACE

@@ -1,4 +1,4 @@
-"""Seeded synthetic inputs for the five workloads of this library.
+"""Seeded synthetic inputs for the workloads of this library.
 
 This module only draws random numbers and rounds them to the storage dtype;
 it holds none of the method's arithmetic, so both the oracle side and the HIP
@@ -15,6 +15,12 @@ Distributions (N(mu, s) means mean mu and standard deviation s):
   self-test shapes.
 * ``vocab_ce``: logits (T x V) = bf16(N(0, 2)), labels uniform in [0, V);
   default T=4096, V=128256 (a Llama-3-sized vocabulary).
+* ``vocab_ce_opts``: as ``vocab_ce`` over V padded columns with labels
+  uniform over the first v_valid, and a fraction (default 1/8) of the
+  positions given the ignore label; the measured case is a 128000-entry
+  vocabulary padded to 128256 with label smoothing 0.1.
+* ``vocab_head``: hidden states h (T x d) ~ N(0, 1) and a vocabulary head
+  W (d x V, or its transpose) ~ N(0, w_std), bf16.
 * ``rank_mlp``: one tensor-parallel rank's share of a GELU MLP in the math
   layout: x (T x d) ~ N(0, 1), w1 (d x f) and w2 (f x d) ~ N(0, 0.02),
   G (T x d) ~ N(0, 1), rounded to bf16.  Llama-3-8B at TP=8 is T=4096,
@@ -64,6 +70,20 @@ def vocab_ce(T=4096, V=128256, seed=0, device="cpu", dtype=torch.bfloat16, std=2
     return logits, labels
 
 
+def vocab_ce_opts(T, V, v_valid, seed=0, device="cpu", dtype=torch.bfloat16, std=2.0, ignore_frac=0.125,
+                  ignore_index=-100):
+    """Logits like ``vocab_ce`` over a row of V columns of which the first
+    v_valid are vocabulary (the padding columns hold the same N(0, std)
+    draws), labels uniform over the vocabulary, and about ignore_frac of the
+    positions labelled ignore_index."""
+    g = _gen(device, seed)
+    logits = _normal((T, V), std, g, device, dtype)
+    labels = torch.randint(0, v_valid, (T,), generator=g, device=device, dtype=torch.int64)
+    drop = torch.rand((T,), generator=g, device=device) < ignore_frac
+    labels[drop] = ignore_index
+    return logits, labels
+
+
 def rank_mlp(T, d, f, seed=0, device="cpu", dtype=torch.bfloat16, w_std=0.02):
     g = _gen(device, seed)
     x = _normal((T, d), 1.0, g, device, dtype)
@@ -100,6 +120,10 @@ CONFIGS = {
     "llama3_8b_tp8_rank_mlp": dict(kind="tp_mlp", tp=1, T=4096, d=4096, f=1792, w_layout="math", dtype="bf16"),
     "llama3_70b_tp8_rank_mlp": dict(kind="tp_mlp", tp=1, T=8192, d=8192, f=3584, w_layout="math", dtype="bf16"),
     "llama3_70b_tp8_inner_gemm": dict(kind="sharded_gemm", M=8192, K=1024, N=8192, parts=(1,), axis="inner", dtype="bf16"),
+    # next: cross-entropy options (a 128000-entry vocabulary padded to 128256, label smoothing 0.1,
+    # one position in eight ignored)
+    "vocab_ce_opts_t4096_v128256_p8": dict(kind="vocab_ce_opts", T=4096, V=128256, v_valid=128000, parts=8,
+                                           label_smoothing=0.1, ignore_frac=0.125, dtype="bf16"),
     # next: the vocabulary-parallel output head in front of the CE (Llama-3-8B sizes)
     "llama3_8b_vocab_head_ce_p8": dict(kind="vocab_head_ce", T=4096, d=4096, V=128256, parts=8, dtype="bf16"),
 }
