@@ -21,7 +21,10 @@ it cites:
   state's gradient summed across the shards;
 * the same page's list of what a real cross-entropy must also handle
   (``ce_options.py``): a padded vocabulary, ignored positions and label
-  smoothing, each checked against an unsharded full-vocabulary reference.
+  smoothing, each checked against an unsharded full-vocabulary reference;
+* the TP lesson page's other element-wise activations and its gate / up
+  column-parallel projections (``mlp_act.py``): tanh and SiLU MLPs and the
+  gated MLP, forward and backward, sharded and unsharded.
 
 Where a method reaches a result that has a plain definition (the unsharded
 product, the unsharded MLP, the unsharded cross-entropy), the oracle used for
@@ -39,6 +42,7 @@ from .mlp import gelu, gelu_prime, to_math_layout, mlp_fwd_bwd, tp_mlp_fwd_bwd, 
 from .ce import cross_entropy, vocab_parallel_ce
 from .head import head_ce, vocab_parallel_head_ce
 from .ce_options import cross_entropy_opts, vocab_parallel_ce_opts
+from .mlp_act import ACTS, act, act_prime, mlp_act_fwd_bwd, tp_mlp_act_fwd_bwd
 
 __all__ = [
     "shard_range", "shard_ranges",
@@ -47,4 +51,5 @@ __all__ = [
     "cross_entropy", "vocab_parallel_ce",
     "head_ce", "vocab_parallel_head_ce",
     "cross_entropy_opts", "vocab_parallel_ce_opts",
+    "ACTS", "act", "act_prime", "mlp_act_fwd_bwd", "tp_mlp_act_fwd_bwd",
 ]
