@@ -39,6 +39,7 @@ INNER = dict(M=8192, K=1024, N=8192)
 CE = dict(T=4096, V=128256, parts=8)
 HEAD = dict(T=4096, d=4096, V=128256, parts=8)
 MLP_8B = dict(T=4096, d=4096, f=1792)
+GATED = dict(T=8192, d=8192, f=3584, act="silu")
 CE_OPTS = dict(T=4096, V=128256, v_valid=128000, parts=8, label_smoothing=0.1, ignore_frac=0.125)
 
 
@@ -189,6 +190,40 @@ def bench_mlp_8b(tpr, workloads, dev, steps):
             "pct_of_bf16_peak": round(100.0 * tflops / PEAK_BF16_TFLOPS, 2), "flop_per_call": flop}
 
 
+def bench_gated_mlp(tpr, dev, steps):
+    """The gated SiLU MLP (gate / up / down) of a Llama-3-70B rank at TP = 8
+    (T=8192, d=8192, f=3584, bf16): nine GEMMs of 2*T*d*f FLOP per call."""
+    import torch
+
+    T, d, f = GATED["T"], GATED["d"], GATED["f"]
+    g = torch.Generator(device=dev)
+    g.manual_seed(12)
+    mk = lambda shape, std: (torch.randn(shape, generator=g, device=dev) * std).bfloat16()
+    x, gy = mk((T, d), 1.0), mk((T, d), 1.0)
+    w1, w3, w2 = mk((d, f), 0.02), mk((d, f), 0.02), mk((f, d), 0.02)
+    out = (torch.empty(T, d, device=dev), torch.empty(T, d, device=dev), torch.empty(d, f, device=dev),
+           torch.empty(f, d, device=dev), torch.empty(d, f, device=dev))
+    ws = torch.empty(tpr.tp_mlp_act_workspace_bytes(1, torch.bfloat16, True, T, d, f), dtype=torch.uint8,
+                     device=dev)
+    call = lambda: tpr.tp_mlp_act_fwd_bwd(1, x, w1, w2, gy, act=GATED["act"], w3=w3, out=out, workspace=ws)
+    for _ in range(2):
+        call()
+    torch.cuda.synchronize()
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(steps)]
+    for e in ev:
+        e[0].record()
+        call()
+        e[1].record()
+    torch.cuda.synchronize()
+    ms = sorted(e[0].elapsed_time(e[1]) for e in ev)
+    flop = 18.0 * T * d * f
+    mean = sum(ms) / len(ms)
+    tflops = flop / (mean * 1e-3) / 1e12
+    return {"config": dict(GATED, dtype="bf16", w_layout="math", gated=True), "steps": steps, "ms": round(mean, 4),
+            "ms_min": round(ms[0], 4), "tflops": round(tflops, 1),
+            "pct_of_bf16_peak": round(100.0 * tflops / PEAK_BF16_TFLOPS, 2), "flop_per_call": flop}
+
+
 def bench_ce_opts(tpr, workloads, dev, steps):
     """The cross-entropy with options: a 128000-entry vocabulary padded to
     128256 columns, 8 shards, label smoothing 0.1, about one position in
@@ -236,6 +271,8 @@ def main():
                     help="timed calls of the 8B-rank MLP fwd+bwd (reported beside the step; 0 = skip)")
     ap.add_argument("--ce-opts-steps", type=int, default=10,
                     help="timed calls of the cross-entropy with options (reported beside the step; 0 = skip)")
+    ap.add_argument("--gated-steps", type=int, default=5,
+                    help="timed calls of the gated SiLU MLP at the 70B rank size (reported beside the step; 0 = skip)")
     ap.add_argument("--traffic-from", nargs=3, metavar=("FETCH_CSV", "WRITE_CSV", "COPY_BYTES"))
     ap.add_argument("--copy-bytes", type=int, default=0,
                     help="also run one plain copy kernel (torch.neg on fp32) of this many bytes before timing, "
@@ -329,6 +366,9 @@ def main():
     mlp_8b = None
     if args.mlp_8b_steps > 0:
         mlp_8b = bench_mlp_8b(tpr, workloads, dev, args.mlp_8b_steps)
+    gated = None
+    if args.gated_steps > 0:
+        gated = bench_gated_mlp(tpr, dev, args.gated_steps)
     ce_opts = None
     if args.ce_opts_steps > 0:
         ce_opts = bench_ce_opts(tpr, workloads, dev, args.ce_opts_steps)
@@ -397,6 +437,8 @@ def main():
         line["mlp_8b_rank"] = mlp_8b
     if ce_opts is not None:
         line["vocab_ce_opts"] = ce_opts
+    if gated is not None:
+        line["gated_silu_mlp_70b_rank"] = gated
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline()
     print(json.dumps(line), flush=True)

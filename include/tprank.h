@@ -64,6 +64,12 @@ extern "C" {
 #define TPR_W_MATH 0   /* w1 is d x f and w2 is f x d: y = gelu(x w1) w2      ([TP] 2.A) */
 #define TPR_W_TORCH 1  /* w1 is (f, d) and w2 is (d, f): y = gelu(x w1^T) w2^T ([TP] 1, solution code) */
 
+/* Element-wise activations of the MLP ([TP] 2.A names GeLU and SiLU; the
+ * [CARDS] demo uses tanh, whose derivative 1 - H^2 its 02 / BACKWARD shows). */
+#define TPR_ACT_GELU 0  /* x Phi(x), exact erf */
+#define TPR_ACT_TANH 1  /* tanh(x) */
+#define TPR_ACT_SILU 2  /* x / (1 + exp(-x)) */
+
 /* ---- shard planning ----------------------------------------------------- */
 /*
  * Half-open index range [*begin, *end) of shard `rank` when `n` indices are
@@ -141,6 +147,42 @@ int tp_mlp_fwd_bwd(int tp, int dtype, int w_layout, int64_t T, int64_t d, int64_
                    const void* x, const void* w1, const void* w2, const void* gy,
                    float* y, float* dx, float* dw1, float* dw2,
                    void* ws, size_t ws_bytes, void* stream);
+
+/* ---- MLP with another activation, or gated (gate / up) --------------- */
+/*
+ * Bytes of workspace tp_mlp_act_fwd_bwd() needs.  Plain (gated == 0): as
+ * tp_mlp_workspace_bytes().  Gated: five T x f buffers in `dtype` (gate and
+ * up pre-activations, H, and their gradients), tp fp32 T x d partials of y
+ * when tp > 1, and 2 tp fp32 T x d partials of dx.  0 for invalid arguments.
+ */
+size_t tp_mlp_act_workspace_bytes(int tp, int dtype, int gated, int64_t T, int64_t d, int64_t f);
+
+/*
+ * [TP] 2.A (the element-wise activation sigma, e.g. GeLU or SiLU, applied
+ * locally on each rank's column block) and its question 1 (gate and up
+ * projections with the activation on the column-parallel side, the down
+ * projection row-parallel); backward as [CARDS] 02 / BACKWARD.
+ *   w3 == NULL: the MLP of tp_mlp_fwd_bwd() with sigma = `act` (TPR_ACT_*;
+ *     sigma' of tanh is 1 - H^2, of SiLU s (1 + x (1 - s)), s the sigmoid).
+ *   w3 != NULL (gated): rank r also owns columns [lo, hi) of the up
+ *     projection W3 (same shape and layout as w1) and
+ *       forward:  A_r = x W1_r;  U_r = x W3_r;  H_r = sigma(A_r) * U_r;
+ *                 Z_r = H_r W2_r;
+ *       backward: dH_r = gy W2_r^T;  dW2_r = H_r^T gy;
+ *                 dA_r = dH_r * U_r * sigma'(A_r);  dU_r = dH_r * sigma(A_r);
+ *                 dW1_r = x^T dA_r;  dW3_r = x^T dU_r;
+ *                 dx_r = dA_r W1_r^T + dU_r W3_r^T;
+ *     then y = sum_r Z_r and dx = sum_r dx_r in rank order.  For TPR_BF16
+ *     A, U, H, dH, dA and dU are rounded to bf16.
+ *   Arguments as tp_mlp_fwd_bwd(), plus act, w3 (NULL or like w1) and dw3
+ *   (fp32 like w1; required when w3 is given).
+ * Errors: SHAPE, PARTITION, DTYPE (dtype or w_layout), VALUE (unknown act),
+ * NULLPTR, WORKSPACE, HIP.
+ */
+int tp_mlp_act_fwd_bwd(int tp, int dtype, int w_layout, int act, int64_t T, int64_t d, int64_t f,
+                       const void* x, const void* w1, const void* w3, const void* w2, const void* gy,
+                       float* y, float* dx, float* dw1, float* dw3, float* dw2,
+                       void* ws, size_t ws_bytes, void* stream);
 
 /* ---- vocabulary-parallel cross-entropy -------------------------------- */
 /*

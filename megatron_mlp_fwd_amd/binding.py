@@ -21,6 +21,7 @@ NO_IGNORE = -(2 ** 63)  # an ignore_index no label takes: every row counts
 AXES = {"rows": 0, "columns": 1, "inner": 2}
 DTYPES = {torch.float32: 0, torch.bfloat16: 1}
 W_LAYOUTS = {"math": 0, "torch": 1}
+ACTS = {"gelu": 0, "tanh": 1, "silu": 2}
 
 _lib = None
 
@@ -31,6 +32,8 @@ _SIGS = {
     "sharded_matmul_fwd_bwd": (_i32, [_i32, _i32, _i32, _i64, _i64, _i64, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
     "tp_mlp_workspace_bytes": (_sz, [_i32, _i32, _i64, _i64, _i64]),
     "tp_mlp_fwd_bwd": (_i32, [_i32, _i32, _i32, _i64, _i64, _i64, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
+    "tp_mlp_act_workspace_bytes": (_sz, [_i32, _i32, _i32, _i64, _i64, _i64]),
+    "tp_mlp_act_fwd_bwd": (_i32, [_i32, _i32, _i32, _i32, _i64, _i64, _i64] + [_vp] * 11 + [_sz, _vp]),
     "vocab_parallel_ce_workspace_bytes": (_sz, [_i32, _i64, _i64]),
     "vocab_parallel_ce_fwd_bwd": (_i32, [_i32, _i32, _i64, _i64, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
     "vocab_parallel_ce_opts_workspace_bytes": (_sz, [_i32, _i64, _i64]),
@@ -188,6 +191,59 @@ def tp_mlp_fwd_bwd(tp, x, w1, w2, gy, w_layout="math", out=None, workspace=None,
         _check(lib.tp_mlp_fwd_bwd(tp, DTYPES[dt], layout, T, d, f, _ptr(x), _ptr(w1), _ptr(w2), _ptr(gy), _ptr(y),
                                   _ptr(dx), _ptr(dw1), _ptr(dw2), _ptr(ws), wsb, _stream(stream)))
     return y, dx, dw1, dw2
+
+
+def tp_mlp_act_workspace_bytes(tp, dtype, gated, T, d, f):
+    return load_library().tp_mlp_act_workspace_bytes(tp, DTYPES[dtype], int(bool(gated)), T, d, f)
+
+
+def tp_mlp_act_fwd_bwd(tp, x, w1, w2, gy, act="gelu", w3=None, w_layout="math", out=None, workspace=None,
+                       stream=None):
+    """MLP over ``tp`` simulated ranks with activation ``act`` ("gelu",
+    "tanh", "silu"), gated by the up projection ``w3`` (same shape and layout
+    as ``w1``) when given.  Returns fp32 (y, dx, dw1, dw2, dw3) with dw3 None
+    when not gated."""
+    lib = load_library()
+    layout = W_LAYOUTS[w_layout]
+    if act not in ACTS:
+        raise ValueError(f"unknown activation {act!r}")
+    dt = x.dtype
+    if dt not in DTYPES:
+        raise ValueError(f"unsupported dtype {dt}")
+    if w1.dim() != 2 or w2.dim() != 2:
+        raise ValueError("w1 and w2 must be 2-D")
+    d, f = (w1.shape[0], w1.shape[1]) if layout == 0 else (w1.shape[1], w1.shape[0])
+    wshape1, wshape2 = ((d, f), (f, d)) if layout == 0 else ((f, d), (d, f))
+    if x.dim() < 1 or x.shape[-1] != d:
+        raise ValueError(f"x must be (..., {d})")
+    T = 1
+    for n in x.shape[:-1]:
+        T *= n
+    dev = x.device
+    xs = tuple(x.shape)
+    _need(x, "x", xs, dt, dev)
+    _need(gy, "gy", xs, dt, dev)
+    _need(w1, "w1", wshape1, dt, dev)
+    _need(w2, "w2", wshape2, dt, dev)
+    gated = w3 is not None
+    if gated:
+        _need(w3, "w3", wshape1, dt, dev)
+    if out is None:
+        out = (torch.empty(xs, device=dev), torch.empty(xs, device=dev), torch.empty(wshape1, device=dev),
+               torch.empty(wshape2, device=dev), torch.empty(wshape1, device=dev) if gated else None)
+    y, dx, dw1, dw2, dw3 = out
+    _need(y, "y", xs, torch.float32, dev)
+    _need(dx, "dx", xs, torch.float32, dev)
+    _need(dw1, "dw1", wshape1, torch.float32, dev)
+    _need(dw2, "dw2", wshape2, torch.float32, dev)
+    if gated:
+        _need(dw3, "dw3", wshape1, torch.float32, dev)
+    ws, wsb = _workspace(lib.tp_mlp_act_workspace_bytes(tp, DTYPES[dt], int(gated), T, d, f), dev, workspace)
+    with torch.cuda.device(dev):
+        _check(lib.tp_mlp_act_fwd_bwd(tp, DTYPES[dt], layout, ACTS[act], T, d, f, _ptr(x), _ptr(w1), _ptr(w3),
+                                      _ptr(w2), _ptr(gy), _ptr(y), _ptr(dx), _ptr(dw1), _ptr(dw3), _ptr(dw2),
+                                      _ptr(ws), wsb, _stream(stream)))
+    return y, dx, dw1, dw2, dw3
 
 
 def vocab_parallel_ce_workspace_bytes(parts, T, V):

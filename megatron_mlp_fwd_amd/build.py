@@ -26,7 +26,7 @@ FLAGS = [
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     f"-I{INCLUDE}", f"-I{CSRC}",
 ]
-SOURCES = ["gemm_bf16.hip", "gemm_bf16_dma.hip", "gemm_f32.hip", "reduce.hip", "vocab_ce.hip", "capi.cpp"]
+SOURCES = ["gemm_bf16.hip", "gemm_bf16_dma.hip", "gemm_f32.hip", "reduce.hip", "vocab_ce.hip", "glu.hip", "capi.cpp"]
 
 
 def _compile(src):

@@ -227,75 +227,70 @@ int sharded_matmul_fwd_bwd(int axis, int parts, int dtype, int64_t M, int64_t K,
 }
 
 // ---------------------------------------------------------------- TP MLP
-size_t tp_mlp_workspace_bytes(int tp, int dtype, int64_t T, int64_t d, int64_t f) {
+namespace {
+
+size_t mlp_workspace(int tp, int dtype, bool gated, int64_t T, int64_t d, int64_t f) {
   if (tp < 1 || !dtype_ok(dtype) || T < 0 || d < 0 || f < 0) return 0;
-  size_t b = 2 * align256((size_t)(T * f * esize(dtype)));
-  if (tp > 1) b += 2 * (size_t)tp * align256((size_t)(T * d * 4));
-  return b;
+  const size_t tf = align256((size_t)(T * f * esize(dtype))), td = align256((size_t)(T * d * 4));
+  if (!gated) return 2 * tf + (tp > 1 ? 2 * (size_t)tp * td : 0);
+  // gate, up, H, dA (dH first), dU; y partials when tp > 1; two dx partials per rank
+  return 5 * tf + (tp > 1 ? (size_t)tp * td : 0) + 2 * (size_t)tp * td;
 }
 
-int tp_mlp_fwd_bwd(int tp, int dtype, int w_layout, int64_t T, int64_t d, int64_t f, const void* x, const void* w1,
-                   const void* w2, const void* gy, float* y, float* dx, float* dw1, float* dw2, void* ws,
-                   size_t ws_bytes, void* stream) {
-  if (!dim_ok(T) || !dim_ok(d) || !dim_ok(f))
-    return fail(TPR_ERR_SHAPE, "T, d, f must be in [0, 2^31) (got %lld, %lld, %lld)", (long long)T, (long long)d,
-                (long long)f);
-  if (tp < 1) return fail(TPR_ERR_PARTITION, "tp must be >= 1 (got %d)", tp);
-  if (!dtype_ok(dtype)) return fail(TPR_ERR_DTYPE, "unknown dtype %d", dtype);
-  if (w_layout != TPR_W_MATH && w_layout != TPR_W_TORCH) return fail(TPR_ERR_DTYPE, "unknown w_layout %d", w_layout);
-  if ((T * d > 0 && (x == nullptr || gy == nullptr || y == nullptr || dx == nullptr)) ||
-      (d * f > 0 && (w1 == nullptr || w2 == nullptr || dw1 == nullptr || dw2 == nullptr)))
-    return fail(TPR_ERR_NULLPTR, "a non-empty input or output pointer is NULL");
-  const size_t need = tp_mlp_workspace_bytes(tp, dtype, T, d, f);
-  if (ws_bytes < need || (need > 0 && ws == nullptr))
-    return fail(TPR_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", need, ws_bytes);
+int check_act(int act) {
+  if (act != TPR_ACT_GELU && act != TPR_ACT_TANH && act != TPR_ACT_SILU)
+    return fail(TPR_ERR_VALUE, "unknown activation %d", act);
+  return TPR_OK;
+}
 
-  hipStream_t s = static_cast<hipStream_t>(stream);
+// Plain MLP: fc1's epilogue writes H = sigma(P) and sigma'(P) from the fp32
+// accumulator; then fc2 (row-parallel) with the two backward products that
+// need only H and gy: dW2 and dZ = (gy W2^T) * sigma'(P) (in place over
+// sigma'(P)); then dW1 and dx.
+int mlp_plain(int tp, int dtype, bool math, int act, int64_t T, int64_t d, int64_t f, const void* x, const void* w1,
+              const void* w2, const void* gy, float* y, float* dx, float* dw1, float* dw2, void* ws, hipStream_t s) {
   const int64_t e = esize(dtype);
   char* wsb = static_cast<char*>(ws);
-  char* pre = wsb;                                            // T x f GELU'(pre-activation), then dZ in place
-  char* act = wsb + align256((size_t)(T * f * e));            // T x f activation
+  char* pre = wsb;                                  // T x f sigma'(pre-activation), then dZ in place
+  char* actv = wsb + align256((size_t)(T * f * e));  // T x f activation
   const int64_t pstride = (int64_t)(align256((size_t)(T * d * 4)) / 4);
   float* zpart = reinterpret_cast<float*>(wsb + 2 * align256((size_t)(T * f * e)));
   float* xpart = zpart + (int64_t)tp * pstride;
   const bool direct = tp == 1;
-  const bool math = w_layout == TPR_W_MATH;
   int nslots = 0;
-  // Launch groups: fc1 | fc2, dW2, dH (independent of each other) | dW1, dx.
-  std::vector<Job> fwd1, mid, last;
-
+  std::vector<Job> fwd1, mid, last;  // launch groups: fc1 | fc2, dW2, dH | dW1, dx
   for (int r = 0; r < tp; ++r) {
     int64_t lo, hi;
     shard_of(f, tp, r, &lo, &hi);
     const int64_t fr = hi - lo;
     if (fr == 0) continue;
     char* Pr = pre + T * lo * e;  // rank-local T x fr blocks
-    char* Hr = act + T * lo * e;
+    char* Hr = actv + T * lo * e;
     float* ydst = direct ? y : zpart + nslots * pstride;
     float* xdst = direct ? dx : xpart + nslots * pstride;
+    tpr::GemmProb p1;
     if (math) {  // w1 d x f, w2 f x d
-      fwd1.push_back(job(prob(x, d, 1, cb(w1) + lo * e, f, 1, Pr, fr, T, fr, d, nullptr, Hr), true, false, tpr::EPI_GELU));
+      p1 = prob(x, d, 1, cb(w1) + lo * e, f, 1, Pr, fr, T, fr, d, nullptr, Hr);
+      p1.act = act;
+      fwd1.push_back(job(p1, true, false, tpr::EPI_ACT));
       mid.push_back(job(prob(Hr, fr, 1, cb(w2) + lo * d * e, d, 1, ydst, d, T, d, fr), true, false, tpr::EPI_F32));
       mid.push_back(job(prob(Hr, 1, fr, gy, d, 1, dw2 + lo * d, d, fr, d, T), false, false, tpr::EPI_F32));
-      mid.push_back(job(prob(gy, d, 1, cb(w2) + lo * d * e, 1, d, Pr, fr, T, fr, d, Pr), true, true, tpr::EPI_DGELU));
+      mid.push_back(job(prob(gy, d, 1, cb(w2) + lo * d * e, 1, d, Pr, fr, T, fr, d, Pr), true, true, tpr::EPI_MUL));
       last.push_back(job(prob(x, 1, d, Pr, fr, 1, dw1 + lo, f, d, fr, T), false, false, tpr::EPI_F32));
       last.push_back(job(prob(Pr, fr, 1, cb(w1) + lo * e, 1, f, xdst, d, T, d, fr), true, true, tpr::EPI_F32));
     } else {  // w1 (f, d), w2 (d, f)
-      fwd1.push_back(job(prob(x, d, 1, cb(w1) + lo * d * e, 1, d, Pr, fr, T, fr, d, nullptr, Hr), true, true, tpr::EPI_GELU));
+      p1 = prob(x, d, 1, cb(w1) + lo * d * e, 1, d, Pr, fr, T, fr, d, nullptr, Hr);
+      p1.act = act;
+      fwd1.push_back(job(p1, true, true, tpr::EPI_ACT));
       mid.push_back(job(prob(Hr, fr, 1, cb(w2) + lo * e, 1, f, ydst, d, T, d, fr), true, true, tpr::EPI_F32));
       mid.push_back(job(prob(gy, 1, d, Hr, fr, 1, dw2 + lo, f, d, fr, T), false, false, tpr::EPI_F32));
-      mid.push_back(job(prob(gy, d, 1, cb(w2) + lo * e, f, 1, Pr, fr, T, fr, d, Pr), true, false, tpr::EPI_DGELU));
+      mid.push_back(job(prob(gy, d, 1, cb(w2) + lo * e, f, 1, Pr, fr, T, fr, d, Pr), true, false, tpr::EPI_MUL));
       last.push_back(job(prob(Pr, 1, fr, x, d, 1, dw1 + lo * d, d, fr, d, T), false, false, tpr::EPI_F32));
       last.push_back(job(prob(Pr, fr, 1, cb(w1) + lo * d * e, d, 1, xdst, d, T, d, fr), true, false, tpr::EPI_F32));
     }
     ++nslots;
   }
-
   hipError_t he;
-  // Forward fc1 (column-parallel GEMM; its epilogue writes H = GELU(P) and
-  // GELU'(P), evaluated from the fp32 accumulator); then fc2 (row-parallel
-  // GEMM) together with the two backward products that need only H and gy:
-  // dW2 and dZ = (gy W2^T) * GELU'(P); then dW1 and dx.
   if ((he = run_jobs(fwd1, dtype, s)) != hipSuccess) return hip_fail(he, "fc1 GEMM");
   if ((he = run_jobs(mid, dtype, s)) != hipSuccess) return hip_fail(he, "fc2 / dW2 / dH GEMMs");
   if ((he = run_jobs(last, dtype, s)) != hipSuccess) return hip_fail(he, "dW1 / dx GEMMs");
@@ -304,6 +299,124 @@ int tp_mlp_fwd_bwd(int tp, int dtype, int w_layout, int64_t T, int64_t d, int64_
   if ((he = finish_sum(dx, T, d, xpart, nslots, pstride, direct, s)) != hipSuccess)
     return hip_fail(he, "dx reduction");
   return TPR_OK;
+}
+
+// Gated MLP: {A_r = X W1_r, U_r = X W3_r} | H = sigma(A) U | {Z_r = H_r W2_r,
+// dW2_r = H_r^T gy, dH_r = gy W2_r^T} | dA = dH U sigma'(A), dU = dH sigma(A)
+// | {dW1_r = X^T dA_r, dW3_r = X^T dU_r, dx_r = dA_r W1_r^T + dU_r W3_r^T}.
+// The two products of dx_r land in two partial slots summed with the ranks'.
+int mlp_gated(int tp, int dtype, bool math, int act, int64_t T, int64_t d, int64_t f, const void* x, const void* w1,
+              const void* w3, const void* w2, const void* gy, float* y, float* dx, float* dw1, float* dw3, float* dw2,
+              void* ws, hipStream_t s) {
+  const int64_t e = esize(dtype);
+  const size_t tf = align256((size_t)(T * f * e));
+  char* wsb = static_cast<char*>(ws);
+  char* Ab = wsb;            // gate pre-activation
+  char* Ub = wsb + tf;       // up projection
+  char* Hb = wsb + 2 * tf;   // sigma(A) U
+  char* dAb = wsb + 3 * tf;  // dH, then dA in place
+  char* dUb = wsb + 4 * tf;
+  const int64_t pstride = (int64_t)(align256((size_t)(T * d * 4)) / 4);
+  float* zpart = reinterpret_cast<float*>(wsb + 5 * tf);
+  float* xpart = zpart + (tp > 1 ? (int64_t)tp * pstride : 0);
+  const bool ydirect = tp == 1;
+  const int raw = dtype == TPR_BF16 ? tpr::EPI_BF16 : tpr::EPI_F32;  // output in the compute dtype
+  int nslots = 0, nx = 0;
+  std::vector<Job> fwd1, mid, last;
+  for (int r = 0; r < tp; ++r) {
+    int64_t lo, hi;
+    shard_of(f, tp, r, &lo, &hi);
+    const int64_t fr = hi - lo;
+    if (fr == 0) continue;
+    char* Ar = Ab + T * lo * e;
+    char* Ur = Ub + T * lo * e;
+    char* Hr = Hb + T * lo * e;
+    char* dAr = dAb + T * lo * e;
+    char* dUr = dUb + T * lo * e;
+    float* ydst = ydirect ? y : zpart + nslots * pstride;
+    float* xg = xpart + (nx++) * pstride;
+    float* xu = xpart + (nx++) * pstride;
+    if (math) {  // w1, w3 d x f, w2 f x d
+      fwd1.push_back(job(prob(x, d, 1, cb(w1) + lo * e, f, 1, Ar, fr, T, fr, d), true, false, raw));
+      fwd1.push_back(job(prob(x, d, 1, cb(w3) + lo * e, f, 1, Ur, fr, T, fr, d), true, false, raw));
+      mid.push_back(job(prob(Hr, fr, 1, cb(w2) + lo * d * e, d, 1, ydst, d, T, d, fr), true, false, tpr::EPI_F32));
+      mid.push_back(job(prob(Hr, 1, fr, gy, d, 1, dw2 + lo * d, d, fr, d, T), false, false, tpr::EPI_F32));
+      mid.push_back(job(prob(gy, d, 1, cb(w2) + lo * d * e, 1, d, dAr, fr, T, fr, d), true, true, raw));
+      last.push_back(job(prob(x, 1, d, dAr, fr, 1, dw1 + lo, f, d, fr, T), false, false, tpr::EPI_F32));
+      last.push_back(job(prob(x, 1, d, dUr, fr, 1, dw3 + lo, f, d, fr, T), false, false, tpr::EPI_F32));
+      last.push_back(job(prob(dAr, fr, 1, cb(w1) + lo * e, 1, f, xg, d, T, d, fr), true, true, tpr::EPI_F32));
+      last.push_back(job(prob(dUr, fr, 1, cb(w3) + lo * e, 1, f, xu, d, T, d, fr), true, true, tpr::EPI_F32));
+    } else {  // w1, w3 (f, d), w2 (d, f)
+      fwd1.push_back(job(prob(x, d, 1, cb(w1) + lo * d * e, 1, d, Ar, fr, T, fr, d), true, true, raw));
+      fwd1.push_back(job(prob(x, d, 1, cb(w3) + lo * d * e, 1, d, Ur, fr, T, fr, d), true, true, raw));
+      mid.push_back(job(prob(Hr, fr, 1, cb(w2) + lo * e, 1, f, ydst, d, T, d, fr), true, true, tpr::EPI_F32));
+      mid.push_back(job(prob(gy, 1, d, Hr, fr, 1, dw2 + lo, f, d, fr, T), false, false, tpr::EPI_F32));
+      mid.push_back(job(prob(gy, d, 1, cb(w2) + lo * e, f, 1, dAr, fr, T, fr, d), true, false, raw));
+      last.push_back(job(prob(dAr, 1, fr, x, d, 1, dw1 + lo * d, d, fr, d, T), false, false, tpr::EPI_F32));
+      last.push_back(job(prob(dUr, 1, fr, x, d, 1, dw3 + lo * d, d, fr, d, T), false, false, tpr::EPI_F32));
+      last.push_back(job(prob(dAr, fr, 1, cb(w1) + lo * d * e, d, 1, xg, d, T, d, fr), true, false, tpr::EPI_F32));
+      last.push_back(job(prob(dUr, fr, 1, cb(w3) + lo * d * e, d, 1, xu, d, T, d, fr), true, false, tpr::EPI_F32));
+    }
+    ++nslots;
+  }
+  hipError_t he;
+  if ((he = run_jobs(fwd1, dtype, s)) != hipSuccess) return hip_fail(he, "gate / up GEMMs");
+  if ((he = tpr::launch_glu_fwd(dtype, Ab, Ub, Hb, T * f, act, s)) != hipSuccess) return hip_fail(he, "gate * up");
+  if ((he = run_jobs(mid, dtype, s)) != hipSuccess) return hip_fail(he, "down / dW2 / dH GEMMs");
+  if ((he = tpr::launch_glu_bwd(dtype, dAb, Ab, Ub, dUb, T * f, act, s)) != hipSuccess)
+    return hip_fail(he, "gate / up gradients");
+  if ((he = run_jobs(last, dtype, s)) != hipSuccess) return hip_fail(he, "dW1 / dW3 / dx GEMMs");
+  if ((he = finish_sum(y, T, d, zpart, nslots, pstride, ydirect, s)) != hipSuccess) return hip_fail(he, "y reduction");
+  if ((he = finish_sum(dx, T, d, xpart, nx, pstride, false, s)) != hipSuccess) return hip_fail(he, "dx reduction");
+  return TPR_OK;
+}
+
+int mlp_checked(int tp, int dtype, int w_layout, int act, int64_t T, int64_t d, int64_t f, const void* x,
+                const void* w1, const void* w3, const void* w2, const void* gy, float* y, float* dx, float* dw1,
+                float* dw3, float* dw2, void* ws, size_t ws_bytes, void* stream) {
+  if (!dim_ok(T) || !dim_ok(d) || !dim_ok(f))
+    return fail(TPR_ERR_SHAPE, "T, d, f must be in [0, 2^31) (got %lld, %lld, %lld)", (long long)T, (long long)d,
+                (long long)f);
+  if (tp < 1) return fail(TPR_ERR_PARTITION, "tp must be >= 1 (got %d)", tp);
+  if (!dtype_ok(dtype)) return fail(TPR_ERR_DTYPE, "unknown dtype %d", dtype);
+  if (w_layout != TPR_W_MATH && w_layout != TPR_W_TORCH) return fail(TPR_ERR_DTYPE, "unknown w_layout %d", w_layout);
+  if (check_act(act) != TPR_OK) return TPR_ERR_VALUE;
+  const bool gated = w3 != nullptr;
+  if ((T * d > 0 && (x == nullptr || gy == nullptr || y == nullptr || dx == nullptr)) ||
+      (d * f > 0 && (w1 == nullptr || w2 == nullptr || dw1 == nullptr || dw2 == nullptr)) ||
+      (gated && d * f > 0 && dw3 == nullptr))
+    return fail(TPR_ERR_NULLPTR, "a non-empty input or output pointer is NULL");
+  const size_t need = mlp_workspace(tp, dtype, gated, T, d, f);
+  if (ws_bytes < need || (need > 0 && ws == nullptr))
+    return fail(TPR_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", need, ws_bytes);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const bool math = w_layout == TPR_W_MATH;
+  if (gated) return mlp_gated(tp, dtype, math, act, T, d, f, x, w1, w3, w2, gy, y, dx, dw1, dw3, dw2, ws, s);
+  return mlp_plain(tp, dtype, math, act, T, d, f, x, w1, w2, gy, y, dx, dw1, dw2, ws, s);
+}
+
+}  // namespace
+
+size_t tp_mlp_workspace_bytes(int tp, int dtype, int64_t T, int64_t d, int64_t f) {
+  return mlp_workspace(tp, dtype, false, T, d, f);
+}
+
+int tp_mlp_fwd_bwd(int tp, int dtype, int w_layout, int64_t T, int64_t d, int64_t f, const void* x, const void* w1,
+                   const void* w2, const void* gy, float* y, float* dx, float* dw1, float* dw2, void* ws,
+                   size_t ws_bytes, void* stream) {
+  return mlp_checked(tp, dtype, w_layout, TPR_ACT_GELU, T, d, f, x, w1, nullptr, w2, gy, y, dx, dw1, nullptr, dw2, ws,
+                     ws_bytes, stream);
+}
+
+size_t tp_mlp_act_workspace_bytes(int tp, int dtype, int gated, int64_t T, int64_t d, int64_t f) {
+  return mlp_workspace(tp, dtype, gated != 0, T, d, f);
+}
+
+int tp_mlp_act_fwd_bwd(int tp, int dtype, int w_layout, int act, int64_t T, int64_t d, int64_t f, const void* x,
+                       const void* w1, const void* w3, const void* w2, const void* gy, float* y, float* dx,
+                       float* dw1, float* dw3, float* dw2, void* ws, size_t ws_bytes, void* stream) {
+  return mlp_checked(tp, dtype, w_layout, act, T, d, f, x, w1, w3, w2, gy, y, dx, dw1, dw3, dw2, ws, ws_bytes,
+                     stream);
 }
 
 // ---------------------------------------------------------------- vocab CE

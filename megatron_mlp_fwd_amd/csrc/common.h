@@ -18,11 +18,12 @@ struct GemmProb {
   const void* A;
   const void* B;
   void* C;
-  const void* aux_in;   // epilogue input (GELU'(pre-activation) for EPI_DGELU)
-  void* aux_out;        // epilogue second output (activation for EPI_GELU)
+  const void* aux_in;   // epilogue input (sigma'(pre-activation) for EPI_MUL)
+  void* aux_out;        // epilogue second output (the activation for EPI_ACT)
   int64_t sa_m, sa_k, sb_k, sb_n, ldc;
   int M, N, K;
   int kind;              // gemm_kind(a_kmajor, b_kmajor, epilogue) for heterogeneous launches
+  int act;               // activation of EPI_ACT (ACT_GELU / ACT_TANH / ACT_SILU)
   int tiles_m, tiles_n;  // filled by the launcher
   int tile_start;        // first flattened block index of this problem
 };
@@ -37,10 +38,13 @@ struct GemmBatch {
 
 enum Epilogue {
   EPI_F32 = 0,    // C (fp32) = acc
-  EPI_GELU = 1,   // C (compute dtype) = gelu'(acc), aux_out = gelu(acc)   [acc = pre-activation]
-  EPI_DGELU = 2,  // C (compute dtype) = acc * aux_in                       [in place allowed]
+  EPI_ACT = 1,   // C (compute dtype) = sigma'(acc), aux_out = sigma(acc)  [acc = pre-activation]
+  EPI_MUL = 2,   // C (compute dtype) = acc * aux_in                       [in place allowed]
   EPI_BF16 = 3,   // C (bf16) = acc, rounded to nearest even
 };
+
+// Element-wise activations (same values as TPR_ACT_* in tprank.h).
+enum Activation { ACT_GELU = 0, ACT_TANH = 1, ACT_SILU = 2 };
 
 constexpr int gemm_kind(bool a_kmajor, bool b_kmajor, int epi) {
   return (a_kmajor ? 1 : 0) | (b_kmajor ? 2 : 0) | (epi << 2);
@@ -63,6 +67,13 @@ hipError_t launch_gemm_f32(GemmBatch& b, bool a_kmajor, bool b_kmajor, int epi, 
 hipError_t launch_reduce_partials(const float* part, int nslots, int64_t stride, float* out, int64_t n,
                                   hipStream_t s);
 hipError_t launch_fill_zero(float* out, int64_t rows, int64_t cols, int64_t ld, hipStream_t s);
+
+// Gated MLP element-wise steps over n contiguous elements of `dtype`
+// (TPR_F32 / TPR_BF16), 16-byte aligned: H = sigma(A) U, and
+// dA = dH U sigma'(A), dU = dH sigma(A) with dA holding dH on entry.
+hipError_t launch_glu_fwd(int dtype, const void* A, const void* U, void* H, int64_t n, int act, hipStream_t s);
+hipError_t launch_glu_bwd(int dtype, void* dA, const void* A, const void* U, void* dU, int64_t n, int act,
+                          hipStream_t s);
 
 // ---------------------------------------------------------------- vocab CE
 struct CeArgs {

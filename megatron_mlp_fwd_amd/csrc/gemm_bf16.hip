@@ -1,5 +1,6 @@
 // bf16 GEMM on the gfx950 matrix cores (v_mfma_f32_16x16x32_bf16), fp32
-// accumulation, with the GELU / GELU' epilogues of the tensor-parallel MLP.
+// accumulation, with the activation / activation-derivative epilogues of the
+// tensor-parallel MLP.
 //
 // Every per-rank product of the sharded GEMM page ("Sharded GEMM与Backprop：
 // 行、列、内维三种切分", 解题路线 steps 1-4) and of the TP lesson's MLP
@@ -135,7 +136,8 @@ __device__ __forceinline__ void mma_stage(const uint16_t* __restrict__ As, const
   }
 }
 
-template <bool AK, bool BKM, bool VEC, int EPI>
+// ACT: the activation of EPI_ACT (one kernel instance per activation).
+template <bool AK, bool BKM, bool VEC, int EPI, int ACT = ACT_GELU>
 __global__ __launch_bounds__(NT, 1) void gemm_bf16_kernel(const GemmBatch batch, int vec_c) {
   __shared__ __attribute__((aligned(16))) uint16_t smem[2 * STAGE];
 
@@ -181,17 +183,28 @@ __global__ __launch_bounds__(NT, 1) void gemm_bf16_kernel(const GemmBatch batch,
     __syncthreads();
   }
 
-  epilogue_via_lds<EPI, WTM, WTN>(reinterpret_cast<float*>(smem), acc, P, m0, n0, wid, wm, wn, lane, vec_c);
+  epilogue_via_lds<EPI, WTM, WTN, ACT>(reinterpret_cast<float*>(smem), acc, P, m0, n0, wid, wm, wn, lane, vec_c);
 }
 
 template <bool AK, bool BKM, bool VEC>
 hipError_t launch_epi(const GemmBatch& b, int epi, int vec_c, hipStream_t s) {
   const dim3 grid(b.total_tiles), block(NT);
+  const int act = b.count > 0 ? b.p[0].act : ACT_GELU;
+  if (epi == EPI_ACT)
+    for (int i = 1; i < b.count; ++i)
+      if (b.p[i].act != act) return hipErrorInvalidValue;  // one activation per launch
   switch (epi) {
     case EPI_F32: hipLaunchKernelGGL((gemm_bf16_kernel<AK, BKM, VEC, EPI_F32>), grid, block, 0, s, b, vec_c); break;
-    case EPI_GELU: hipLaunchKernelGGL((gemm_bf16_kernel<AK, BKM, VEC, EPI_GELU>), grid, block, 0, s, b, vec_c); break;
+    case EPI_ACT:
+      if (act == ACT_TANH)
+        hipLaunchKernelGGL((gemm_bf16_kernel<AK, BKM, VEC, EPI_ACT, ACT_TANH>), grid, block, 0, s, b, vec_c);
+      else if (act == ACT_SILU)
+        hipLaunchKernelGGL((gemm_bf16_kernel<AK, BKM, VEC, EPI_ACT, ACT_SILU>), grid, block, 0, s, b, vec_c);
+      else
+        hipLaunchKernelGGL((gemm_bf16_kernel<AK, BKM, VEC, EPI_ACT, ACT_GELU>), grid, block, 0, s, b, vec_c);
+      break;
     case EPI_BF16: hipLaunchKernelGGL((gemm_bf16_kernel<AK, BKM, VEC, EPI_BF16>), grid, block, 0, s, b, vec_c); break;
-    default: hipLaunchKernelGGL((gemm_bf16_kernel<AK, BKM, VEC, EPI_DGELU>), grid, block, 0, s, b, vec_c); break;
+    default: hipLaunchKernelGGL((gemm_bf16_kernel<AK, BKM, VEC, EPI_MUL>), grid, block, 0, s, b, vec_c); break;
   }
   return hipGetLastError();
 }
@@ -216,8 +229,8 @@ hipError_t launch_gemm_bf16(GemmBatch& b, bool a_kmajor, bool b_kmajor, int epi,
     vec = vec && aligned(p.A, 16) && aligned(p.B, 16) && a_ld % 8 == 0 && b_ld % 8 == 0 && a_ext % 8 == 0 &&
           b_ext % 8 == 0;
     const int cbytes = epi == EPI_F32 ? 16 : 8;
-    vec_c = vec_c && aligned(p.C, cbytes) && p.ldc % 4 == 0 && (epi != EPI_GELU || aligned(p.aux_out, 8)) &&
-            (epi != EPI_DGELU || aligned(p.aux_in, 8));
+    vec_c = vec_c && aligned(p.C, cbytes) && p.ldc % 4 == 0 && (epi != EPI_ACT || aligned(p.aux_out, 8)) &&
+            (epi != EPI_MUL || aligned(p.aux_in, 8));
   }
   b.total_tiles = total;
   if (total == 0) return hipSuccess;

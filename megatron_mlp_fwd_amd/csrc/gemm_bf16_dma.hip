@@ -218,7 +218,7 @@ __device__ __forceinline__ void read_one(Frag<KMAJ>& fr, const FragAddr<KMAJ>& f
 }
 
 // One 256 x 256 output tile of problem P.
-template <bool AK, bool BKM, int EPI>
+template <bool AK, bool BKM, int EPI, bool ACT_DISPATCH = false>
 __device__ __forceinline__ void gemm_tile(const GemmProb& P, int tm, int tn, uint8_t* smem_raw, int vec_c) {
   lds_u8* smem = (lds_u8*)smem_raw;
   const uint32_t lds0 = (uint32_t)(uintptr_t)smem;
@@ -337,13 +337,26 @@ __device__ __forceinline__ void gemm_tile(const GemmProb& P, int tm, int tn, uin
   }
   mfma_drain();
   __syncthreads();
-  epilogue_via_lds<EPI, WT, WT>(reinterpret_cast<float*>(smem_raw), acc, P, m0, n0, wid, wm, wn, lane, vec_c);
+  float* stage = reinterpret_cast<float*>(smem_raw);
+  if constexpr (EPI == EPI_ACT && ACT_DISPATCH) {  // activation chosen once per tile
+    if (P.act == ACT_TANH)
+      epilogue_via_lds<EPI, WT, WT, ACT_TANH>(stage, acc, P, m0, n0, wid, wm, wn, lane, vec_c);
+    else if (P.act == ACT_SILU)
+      epilogue_via_lds<EPI, WT, WT, ACT_SILU>(stage, acc, P, m0, n0, wid, wm, wn, lane, vec_c);
+    else
+      epilogue_via_lds<EPI, WT, WT, ACT_GELU>(stage, acc, P, m0, n0, wid, wm, wn, lane, vec_c);
+  } else {
+    epilogue_via_lds<EPI, WT, WT>(stage, acc, P, m0, n0, wid, wm, wn, lane, vec_c);
+  }
 }
 
 // Block -> (problem, tile).  Every problem's tiles start at a multiple of 8
 // blocks (padding blocks exit), so a block's XCD (blockIdx % 8, the hardware's
 // round-robin) is its position within the problem modulo 8; each XCD gets one
 // contiguous run of the problem's tiles, walked in grouped raster order.
+// ALT_ACT: the instance for batches of activation epilogues other than GELU
+// (EPI_ACT problems only); the main instance keeps GELU as its one activation.
+template <bool ALT_ACT>
 __global__ __launch_bounds__(NTH, 1) void gemm_bf16_dma_kernel(const GemmBatch batch) {
   __shared__ __attribute__((aligned(1024))) uint8_t smem_raw[2 * STAGE_BYTES];
   const int bid = blockIdx.x;
@@ -363,15 +376,23 @@ __global__ __launch_bounds__(NTH, 1) void gemm_bf16_dma_kernel(const GemmBatch b
   local %= per_group;
   const int tm = first_m + local % gsize, tn = local / gsize;
   const int vec_c = P.kind >> 8;
+  if constexpr (ALT_ACT) {
+    switch (P.kind & 0xff) {
+      case gemm_kind(true, false, EPI_ACT): gemm_tile<true, false, EPI_ACT, true>(P, tm, tn, smem_raw, vec_c); break;
+      case gemm_kind(true, true, EPI_ACT): gemm_tile<true, true, EPI_ACT, true>(P, tm, tn, smem_raw, vec_c); break;
+      default: break;  // the launcher sends only activation problems here
+    }
+    return;
+  }
   switch (P.kind & 0xff) {
     case gemm_kind(true, false, EPI_F32): gemm_tile<true, false, EPI_F32>(P, tm, tn, smem_raw, vec_c); break;
     case gemm_kind(true, true, EPI_F32): gemm_tile<true, true, EPI_F32>(P, tm, tn, smem_raw, vec_c); break;
     case gemm_kind(false, false, EPI_F32): gemm_tile<false, false, EPI_F32>(P, tm, tn, smem_raw, vec_c); break;
     case gemm_kind(false, true, EPI_F32): gemm_tile<false, true, EPI_F32>(P, tm, tn, smem_raw, vec_c); break;
-    case gemm_kind(true, false, EPI_GELU): gemm_tile<true, false, EPI_GELU>(P, tm, tn, smem_raw, vec_c); break;
-    case gemm_kind(true, true, EPI_GELU): gemm_tile<true, true, EPI_GELU>(P, tm, tn, smem_raw, vec_c); break;
-    case gemm_kind(true, false, EPI_DGELU): gemm_tile<true, false, EPI_DGELU>(P, tm, tn, smem_raw, vec_c); break;
-    case gemm_kind(true, true, EPI_DGELU): gemm_tile<true, true, EPI_DGELU>(P, tm, tn, smem_raw, vec_c); break;
+    case gemm_kind(true, false, EPI_ACT): gemm_tile<true, false, EPI_ACT>(P, tm, tn, smem_raw, vec_c); break;
+    case gemm_kind(true, true, EPI_ACT): gemm_tile<true, true, EPI_ACT>(P, tm, tn, smem_raw, vec_c); break;
+    case gemm_kind(true, false, EPI_MUL): gemm_tile<true, false, EPI_MUL>(P, tm, tn, smem_raw, vec_c); break;
+    case gemm_kind(true, true, EPI_MUL): gemm_tile<true, true, EPI_MUL>(P, tm, tn, smem_raw, vec_c); break;
     case gemm_kind(true, false, EPI_BF16): gemm_tile<true, false, EPI_BF16>(P, tm, tn, smem_raw, vec_c); break;
     case gemm_kind(true, true, EPI_BF16): gemm_tile<true, true, EPI_BF16>(P, tm, tn, smem_raw, vec_c); break;
     default: break;  // layouts the library never issues with these epilogues
@@ -386,7 +407,7 @@ bool aligned(const void* p, int bytes) { return (reinterpret_cast<uintptr_t>(p) 
 // (whole MFMA steps; a last half slab is handled), 16-byte aligned rows along
 // each operand's contiguous dimension, an extent along it that is a multiple
 // of 8 elements, operand byte ranges that the 32-bit buffer offsets can
-// address, and a (layout, epilogue) pair the kernel instantiates (the GELU
+// address, and a (layout, epilogue) pair the kernel instantiates (the activation
 // and bf16-output epilogues need a k-major A).
 bool gemm_bf16_dma_eligible(const GemmProb& p, bool a_kmajor, bool b_kmajor, int epi) {
   if (p.M <= 0 || p.N <= 0 || p.K <= 0 || p.K % 32 != 0) return false;
@@ -414,13 +435,23 @@ hipError_t launch_gemm_bf16_dma(GemmBatch& b, hipStream_t s) {
     p.tile_start = total;
     total += ((p.tiles_m * p.tiles_n + 7) / 8) * 8;
     const int cbytes = epi == EPI_F32 ? 16 : 8;
-    const bool vec_c = aligned(p.C, cbytes) && p.ldc % 4 == 0 && (epi != EPI_GELU || aligned(p.aux_out, 8)) &&
-                       (epi != EPI_DGELU || aligned(p.aux_in, 8));
+    const bool vec_c = aligned(p.C, cbytes) && p.ldc % 4 == 0 && (epi != EPI_ACT || aligned(p.aux_out, 8)) &&
+                       (epi != EPI_MUL || aligned(p.aux_in, 8));
     p.kind = (p.kind & 0xff) | (vec_c ? 0x100 : 0);
   }
   b.total_tiles = total;
   if (total == 0) return hipSuccess;
-  hipLaunchKernelGGL(gemm_bf16_dma_kernel, dim3(total), dim3(NTH), 0, s, b);
+  bool alt = false, other = false;
+  for (int i = 0; i < b.count; ++i) {
+    const int epi = (b.p[i].kind >> 2) & 3;
+    alt |= epi == EPI_ACT && b.p[i].act != ACT_GELU;
+    other |= epi != EPI_ACT;
+  }
+  if (alt && other) return hipErrorInvalidValue;  // such batches must hold activation problems only
+  if (alt)
+    hipLaunchKernelGGL(gemm_bf16_dma_kernel<true>, dim3(total), dim3(NTH), 0, s, b);
+  else
+    hipLaunchKernelGGL(gemm_bf16_dma_kernel<false>, dim3(total), dim3(NTH), 0, s, b);
   return hipGetLastError();
 }
 

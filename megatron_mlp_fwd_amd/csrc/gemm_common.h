@@ -1,11 +1,12 @@
 // Device-side pieces shared by the bf16 MFMA GEMM kernels: vector types, bf16
-// packing, the exact-erf GELU and its derivative, the block -> tile mapping and
+// packing, the block -> tile mapping and
 // the epilogue (staged through LDS so that stores are row-contiguous).
 #pragma once
 
 #include <type_traits>
 
 #include "common.h"
+#include "activation.h"
 
 namespace tpr {
 namespace gemm {
@@ -40,31 +41,6 @@ __device__ __forceinline__ uint32_t pack_bf16(float a, float b) {
 __device__ __forceinline__ float bf_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
 
-// The exact-erf GELU x Phi(x) and its derivative Phi(x) + x phi(x) for the
-// bf16 kernels, whose pre-activation and results are rounded to bf16.  Phi
-// comes from the Abramowitz-Stegun 7.1.26 (Hastings) form of erfc,
-// erfc(z) = (a1 t + ... + a5 t^5) exp(-z^2), t = 1 / (1 + p z), z >= 0, whose
-// error is below 1.5e-7; evaluated in fp32 the error in Phi, gelu and gelu'
-// stays below 5e-7 absolute (and below 6e-5 relative for gelu at
-// 0.01 < |x| < 3), far under bf16's 2^-8.  exp(-x^2/2) is shared by erfc and
-// phi.  Costs about 15 VALU operations instead of a full-precision erfcf.
-struct PhiExp {
-  float Phi;  // Phi(x)
-  float e;    // exp(-x^2 / 2)
-};
-__device__ __forceinline__ PhiExp phi_exp(float x) {
-  const float z = fabsf(x) * 0.70710678118654752f;
-  const float t = __builtin_amdgcn_rcpf(fmaf(0.3275911f, z, 1.0f));
-  float p = fmaf(t, 1.061405429f, -1.453152027f);
-  p = fmaf(t, p, 1.421413741f);
-  p = fmaf(t, p, -0.284496736f);
-  p = fmaf(t, p, 0.254829592f);
-  const float e = __builtin_amdgcn_exp2f(-0.72134752044448170f * x * x);  // 1 / (2 ln 2)
-  const float q = 0.5f * p * t * e;  // Phi(-|x|)
-  return PhiExp{x >= 0.f ? 1.f - q : q, e};
-}
-
-
 // Workgroups are handed to the 8 XCDs round-robin; renumber so that each XCD
 // walks a contiguous range of tiles (neighbouring tiles share its L2).
 __device__ __forceinline__ int xcd_remap(int bid, int total) {
@@ -93,9 +69,9 @@ __device__ __forceinline__ TileCoord locate_tile(const GemmBatch& batch) {
 }
 
 // Apply the epilogue to four consecutive outputs C[m][n .. n+3] (off = m*ldc+n).
-// For EPI_DGELU, `pre` holds the four bf16 values gelu'(P) when the caller
+// For EPI_MUL, `pre` holds the four bf16 values sigma'(P) when the caller
 // prefetched them (full vector rows); otherwise they are loaded here.
-template <int EPI>
+template <int EPI, int ACT = ACT_GELU>
 __device__ __forceinline__ void epilogue_store(const GemmProb& P, floatx4 v, int64_t off, int n, int N, int vec_c,
                                                u32x2 pre = u32x2{0u, 0u}) {
   const bool full = vec_c && (n + 3 < N);
@@ -110,17 +86,18 @@ __device__ __forceinline__ void epilogue_store(const GemmProb& P, floatx4 v, int
       for (int r = 0; r < 4; ++r)
         if (n + r < N) __builtin_nontemporal_store(v[r], c + r);
     }
-  } else if constexpr (EPI == EPI_GELU) {
-    // acc is the pre-activation P: the activation H = gelu(P) is the next
-    // GEMM's operand and gelu'(P), evaluated here from the fp32 accumulator,
+  } else if constexpr (EPI == EPI_ACT) {
+    // acc is the pre-activation P: the activation H = sigma(P) is the next
+    // GEMM's operand and sigma'(P), evaluated here from the fp32 accumulator,
     // is all the backward pass needs of P.
     uint16_t* c = static_cast<uint16_t*>(P.C) + off;
     uint16_t* h = static_cast<uint16_t*>(P.aux_out) + off;
     floatx4 gv, dv;
     for (int r = 0; r < 4; ++r) {
-      const PhiExp q = phi_exp(v[r]);
-      gv[r] = v[r] * q.Phi;
-      dv[r] = fmaf(0.39894228040143268f * v[r], q.e, q.Phi);
+      float a, da;
+      act_fast<ACT>(v[r], a, da);
+      gv[r] = a;
+      dv[r] = da;
     }
     if (full) {
       *reinterpret_cast<u32x2*>(c) = u32x2{pack_bf16(dv[0], dv[1]), pack_bf16(dv[2], dv[3])};
@@ -140,7 +117,7 @@ __device__ __forceinline__ void epilogue_store(const GemmProb& P, floatx4 v, int
       for (int r = 0; r < 4; ++r)
         if (n + r < N) c[r] = __builtin_bit_cast(uint16_t, (__bf16)v[r]);
     }
-  } else {  // EPI_DGELU: C = acc * gelu'(P), gelu'(P) read from aux_in (may alias C)
+  } else {  // EPI_MUL: C = acc * sigma'(P), sigma'(P) read from aux_in (may alias C)
     uint16_t* c = static_cast<uint16_t*>(P.C) + off;
     if (full) {
       v[0] *= bf_lo(pre[0]);
@@ -160,10 +137,10 @@ __device__ __forceinline__ void epilogue_store(const GemmProb& P, floatx4 v, int
 // wave).  Pass q moves MFMA blocks mi = 2q, 2q+1 of every wave (a 32 x TN_
 // region per wave) into LDS, then each wave reads its region back
 // row-contiguously and applies the epilogue with coalesced stores.  For
-// EPI_DGELU the tile's gelu'(P) values are loaded before the first exchange.  The wave (wm, wn) owns rows wm*TM_ .. and
+// EPI_MUL the tile's sigma'(P) values are loaded before the first exchange.  The wave (wm, wn) owns rows wm*TM_ .. and
 // columns wn*TN_ .. of the block tile, and acc[ni][mi] holds
 // C[m0 + wm*TM_ + mi*16 + lane%16][n0 + wn*TN_ + ni*16 + 4*(lane/16) + r].
-template <int EPI, int TM_, int TN_>
+template <int EPI, int TM_, int TN_, int ACT = ACT_GELU>
 __device__ __forceinline__ void epilogue_via_lds(float* stage, const floatx4 (&acc)[TN_ / 16][TM_ / 16],
                                                  const GemmProb& P, int m0, int n0, int wid, int wm, int wn,
                                                  int lane, int vec_c) {
@@ -177,12 +154,12 @@ __device__ __forceinline__ void epilogue_via_lds(float* stage, const floatx4 (&a
   const int col = 4 * (lane % LANES_PER_ROW);
   const int n = n0 + wn * TN_ + col;
   const bool vec_n = vec_c && n + 3 < N;
-  // For EPI_DGELU the whole tile's gelu'(P) values (TM_/32 passes x ITS
+  // For EPI_MUL the whole tile's sigma'(P) values (TM_/32 passes x ITS
   // loads per lane) are requested before the first pass, so their latency
   // overlaps the LDS exchanges instead of stalling each pass.
-  constexpr int NPRE = EPI == EPI_DGELU ? (TM_ / 32) * ITS : 1;
+  constexpr int NPRE = EPI == EPI_MUL ? (TM_ / 32) * ITS : 1;
   u32x2 pre[NPRE];
-  if constexpr (EPI == EPI_DGELU) {
+  if constexpr (EPI == EPI_MUL) {
 #pragma unroll
     for (int i = 0; i < NPRE; ++i) {
       const int m = m0 + wm * TM_ + 32 * (i / ITS) + lane / LANES_PER_ROW + ROWS_PER_IT * (i % ITS);
@@ -212,10 +189,10 @@ __device__ __forceinline__ void epilogue_via_lds(float* stage, const floatx4 (&a
     for (int it = 0; it < ITS; ++it) {
       const int m = mbase + ROWS_PER_IT * it;
       if (m < M && n < N) {
-        if constexpr (EPI == EPI_DGELU)
-          epilogue_store<EPI>(P, vals[it], (int64_t)m * ldc + n, n, N, vec_c, pre[q * ITS + it]);
+        if constexpr (EPI == EPI_MUL)
+          epilogue_store<EPI, ACT>(P, vals[it], (int64_t)m * ldc + n, n, N, vec_c, pre[q * ITS + it]);
         else
-          epilogue_store<EPI>(P, vals[it], (int64_t)m * ldc + n, n, N, vec_c);
+          epilogue_store<EPI, ACT>(P, vals[it], (int64_t)m * ldc + n, n, N, vec_c);
       }
     }
     __syncthreads();

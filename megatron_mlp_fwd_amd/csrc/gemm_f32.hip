@@ -6,17 +6,12 @@
 // plain LDS-tiled SIMT GEMM: 64 x 64 block tile, 16-deep k slabs, 256
 // threads each owning a 4 x 4 patch, fp32 FMA accumulation in a fixed k
 // order.  Any operand layout is read through its strides.
-#include "common.h"
+#include "activation.h"
 
 namespace tpr {
 namespace {
 
 constexpr int TBM = 64, TBN = 64, TBK = 16;
-
-__device__ __forceinline__ float gelu_f(float x) { return 0.5f * x * erfcf(-0.70710678118654752f * x); }
-__device__ __forceinline__ float gelu_prime_f(float x) {
-  return 0.5f * erfcf(-0.70710678118654752f * x) + 0.39894228040143268f * x * expf(-0.5f * x * x);
-}
 
 template <int EPI>
 __global__ __launch_bounds__(256) void gemm_f32_kernel(const GemmBatch batch, int a_kmajor, int b_kmajor) {
@@ -80,10 +75,12 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(const GemmBatch batch, in
       const float v = acc[i][j];
       if constexpr (EPI == EPI_F32) {
         static_cast<float*>(P.C)[off] = v;
-      } else if constexpr (EPI == EPI_GELU) {  // v is the pre-activation
-        static_cast<float*>(P.C)[off] = gelu_prime_f(v);
-        static_cast<float*>(P.aux_out)[off] = gelu_f(v);
-      } else {  // aux_in holds gelu'(pre-activation)
+      } else if constexpr (EPI == EPI_ACT) {  // v is the pre-activation
+        float a, da;
+        act_eval_f32(P.act, v, a, da);
+        static_cast<float*>(P.C)[off] = da;
+        static_cast<float*>(P.aux_out)[off] = a;
+      } else {  // aux_in holds sigma'(pre-activation)
         static_cast<float*>(P.C)[off] = v * static_cast<const float*>(P.aux_in)[off];
       }
     }
@@ -107,8 +104,8 @@ hipError_t launch_gemm_f32(GemmBatch& b, bool a_kmajor, bool b_kmajor, int epi, 
   const int ak = a_kmajor ? 1 : 0, bk = b_kmajor ? 1 : 0;
   switch (epi) {
     case EPI_F32: hipLaunchKernelGGL(gemm_f32_kernel<EPI_F32>, grid, block, 0, s, b, ak, bk); break;
-    case EPI_GELU: hipLaunchKernelGGL(gemm_f32_kernel<EPI_GELU>, grid, block, 0, s, b, ak, bk); break;
-    default: hipLaunchKernelGGL(gemm_f32_kernel<EPI_DGELU>, grid, block, 0, s, b, ak, bk); break;
+    case EPI_ACT: hipLaunchKernelGGL(gemm_f32_kernel<EPI_ACT>, grid, block, 0, s, b, ak, bk); break;
+    default: hipLaunchKernelGGL(gemm_f32_kernel<EPI_MUL>, grid, block, 0, s, b, ak, bk); break;
   }
   return hipGetLastError();
 }

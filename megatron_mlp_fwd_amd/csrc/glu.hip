@@ -1,0 +1,173 @@
+// Element-wise steps of the gated (gate / up) MLP.
+//
+// TP lesson page ("第 6 课：张量并行 TP"), question 1: the gate and up
+// projections and the activation sit on the column-parallel side, so each
+// rank owns matching column blocks of A = X W1 (gate) and U = X W3 (up) and
+// combines them locally:
+//   forward   H  = sigma(A) * U
+//   backward  dA = dH * U * sigma'(A),   dU = dH * sigma(A)
+// (the multi-card tensor page's 02 / BACKWARD rule G_Z = G_H * sigma',
+// applied to both factors of the product).  The rank blocks are contiguous in
+// one T x f buffer, so one launch covers every rank.  Memory bound: 16-byte
+// vectors of 8 bf16 (or 4 fp32) per thread and iteration, a scalar tail.
+#include "activation.h"
+
+namespace tpr {
+namespace {
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ float bf(uint16_t h) { return __uint_as_float((uint32_t)h << 16); }
+__device__ __forceinline__ uint16_t to_bf(float x) { return __builtin_bit_cast(uint16_t, (__bf16)x); }
+__device__ __forceinline__ float bf_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+__device__ __forceinline__ uint32_t pack2(float a, float b) { return (uint32_t)to_bf(a) | ((uint32_t)to_bf(b) << 16); }
+
+// bf16: fast fp32 activations (results rounded to bf16 anyway).
+__global__ __launch_bounds__(256) void glu_fwd_bf16(const uint16_t* __restrict__ A, const uint16_t* __restrict__ U,
+                                                    uint16_t* __restrict__ H, int64_t n, int act) {
+  const int64_t nv = n / 8;
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < nv; i += stride) {
+    const u32x4 a = reinterpret_cast<const u32x4*>(A)[i];
+    const u32x4 u = reinterpret_cast<const u32x4*>(U)[i];
+    u32x4 h;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      float s0, d0, s1, d1;
+      act_eval(act, bf_lo(a[q]), s0, d0);
+      act_eval(act, bf_hi(a[q]), s1, d1);
+      h[q] = pack2(s0 * bf_lo(u[q]), s1 * bf_hi(u[q]));
+    }
+    reinterpret_cast<u32x4*>(H)[i] = h;
+  }
+  const int64_t t = 8 * nv + blockIdx.x * (int64_t)blockDim.x + threadIdx.x;
+  if (t < n) {
+    float s, ds;
+    act_eval(act, bf(A[t]), s, ds);
+    H[t] = to_bf(s * bf(U[t]));
+  }
+}
+
+// dA is read as dH and overwritten in place.
+__global__ __launch_bounds__(256) void glu_bwd_bf16(uint16_t* __restrict__ dA, const uint16_t* __restrict__ A,
+                                                    const uint16_t* __restrict__ U, uint16_t* __restrict__ dU,
+                                                    int64_t n, int act) {
+  const int64_t nv = n / 8;
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < nv; i += stride) {
+    const u32x4 g = reinterpret_cast<const u32x4*>(dA)[i];
+    const u32x4 a = reinterpret_cast<const u32x4*>(A)[i];
+    const u32x4 u = reinterpret_cast<const u32x4*>(U)[i];
+    u32x4 ga, gu;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      float s0, d0, s1, d1;
+      act_eval(act, bf_lo(a[q]), s0, d0);
+      act_eval(act, bf_hi(a[q]), s1, d1);
+      const float g0 = bf_lo(g[q]), g1 = bf_hi(g[q]);
+      ga[q] = pack2(g0 * bf_lo(u[q]) * d0, g1 * bf_hi(u[q]) * d1);
+      gu[q] = pack2(g0 * s0, g1 * s1);
+    }
+    reinterpret_cast<u32x4*>(dA)[i] = ga;
+    reinterpret_cast<u32x4*>(dU)[i] = gu;
+  }
+  const int64_t t = 8 * nv + blockIdx.x * (int64_t)blockDim.x + threadIdx.x;
+  if (t < n) {
+    float s, ds;
+    act_eval(act, bf(A[t]), s, ds);
+    const float g = bf(dA[t]);
+    dA[t] = to_bf(g * bf(U[t]) * ds);
+    dU[t] = to_bf(g * s);
+  }
+}
+
+// fp32: full-precision activations.
+__global__ __launch_bounds__(256) void glu_fwd_f32(const float* __restrict__ A, const float* __restrict__ U,
+                                                   float* __restrict__ H, int64_t n, int act) {
+  const int64_t nv = n / 4;
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < nv; i += stride) {
+    const f32x4 a = reinterpret_cast<const f32x4*>(A)[i];
+    const f32x4 u = reinterpret_cast<const f32x4*>(U)[i];
+    f32x4 h;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      float s, ds;
+      act_eval_f32(act, a[q], s, ds);
+      h[q] = s * u[q];
+    }
+    reinterpret_cast<f32x4*>(H)[i] = h;
+  }
+  const int64_t t = 4 * nv + blockIdx.x * (int64_t)blockDim.x + threadIdx.x;
+  if (t < n) {
+    float s, ds;
+    act_eval_f32(act, A[t], s, ds);
+    H[t] = s * U[t];
+  }
+}
+
+__global__ __launch_bounds__(256) void glu_bwd_f32(float* __restrict__ dA, const float* __restrict__ A,
+                                                   const float* __restrict__ U, float* __restrict__ dU, int64_t n,
+                                                   int act) {
+  const int64_t nv = n / 4;
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < nv; i += stride) {
+    const f32x4 g = reinterpret_cast<const f32x4*>(dA)[i];
+    const f32x4 a = reinterpret_cast<const f32x4*>(A)[i];
+    const f32x4 u = reinterpret_cast<const f32x4*>(U)[i];
+    f32x4 ga, gu;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      float s, ds;
+      act_eval_f32(act, a[q], s, ds);
+      ga[q] = g[q] * u[q] * ds;
+      gu[q] = g[q] * s;
+    }
+    reinterpret_cast<f32x4*>(dA)[i] = ga;
+    reinterpret_cast<f32x4*>(dU)[i] = gu;
+  }
+  const int64_t t = 4 * nv + blockIdx.x * (int64_t)blockDim.x + threadIdx.x;
+  if (t < n) {
+    float s, ds;
+    act_eval_f32(act, A[t], s, ds);
+    const float g = dA[t];
+    dA[t] = g * U[t] * ds;
+    dU[t] = g * s;
+  }
+}
+
+unsigned grid_for(int64_t nvec) {
+  const int64_t b = (nvec + 255) / 256;
+  return (unsigned)(b < 1 ? 1 : (b > 4096 ? 4096 : b));
+}
+
+}  // namespace
+
+// Buffers are 16-byte aligned and hold n contiguous elements of `dtype`.
+hipError_t launch_glu_fwd(int dtype, const void* A, const void* U, void* H, int64_t n, int act, hipStream_t s) {
+  if (n <= 0) return hipSuccess;
+  if (dtype == 1)
+    hipLaunchKernelGGL(glu_fwd_bf16, dim3(grid_for(n / 8)), dim3(256), 0, s, static_cast<const uint16_t*>(A),
+                       static_cast<const uint16_t*>(U), static_cast<uint16_t*>(H), n, act);
+  else
+    hipLaunchKernelGGL(glu_fwd_f32, dim3(grid_for(n / 4)), dim3(256), 0, s, static_cast<const float*>(A),
+                       static_cast<const float*>(U), static_cast<float*>(H), n, act);
+  return hipGetLastError();
+}
+
+hipError_t launch_glu_bwd(int dtype, void* dA, const void* A, const void* U, void* dU, int64_t n, int act,
+                          hipStream_t s) {
+  if (n <= 0) return hipSuccess;
+  if (dtype == 1)
+    hipLaunchKernelGGL(glu_bwd_bf16, dim3(grid_for(n / 8)), dim3(256), 0, s, static_cast<uint16_t*>(dA),
+                       static_cast<const uint16_t*>(A), static_cast<const uint16_t*>(U), static_cast<uint16_t*>(dU),
+                       n, act);
+  else
+    hipLaunchKernelGGL(glu_bwd_f32, dim3(grid_for(n / 4)), dim3(256), 0, s, static_cast<float*>(dA),
+                       static_cast<const float*>(A), static_cast<const float*>(U), static_cast<float*>(dU), n, act);
+  return hipGetLastError();
+}
+
+}  // namespace tpr

@@ -42,7 +42,7 @@ from .mlp import gelu, gelu_prime, to_math_layout, mlp_fwd_bwd, tp_mlp_fwd_bwd, 
 from .ce import cross_entropy, vocab_parallel_ce
 from .head import head_ce, vocab_parallel_head_ce
 from .ce_options import cross_entropy_opts, vocab_parallel_ce_opts
-from .mlp_act import ACTS, act, act_prime, mlp_act_fwd_bwd, tp_mlp_act_fwd_bwd
+from .mlp_act import ACTS, act, act_prime, mlp_act_fwd_bwd, mlp_act_sampled, tp_mlp_act_fwd_bwd
 
 __all__ = [
     "shard_range", "shard_ranges",
@@ -51,5 +51,5 @@ __all__ = [
     "cross_entropy", "vocab_parallel_ce",
     "head_ce", "vocab_parallel_head_ce",
     "cross_entropy_opts", "vocab_parallel_ce_opts",
-    "ACTS", "act", "act_prime", "mlp_act_fwd_bwd", "tp_mlp_act_fwd_bwd",
+    "ACTS", "act", "act_prime", "mlp_act_fwd_bwd", "mlp_act_sampled", "tp_mlp_act_fwd_bwd",
 ]

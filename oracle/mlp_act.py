@@ -163,3 +163,40 @@ def tp_mlp_act_fwd_bwd(x, w1, w2, gy, tp, act_name, w3=None, w_layout="math"):
         dW2[lo:hi] = H.T @ G
     shape = np.shape(x)
     return (Y.reshape(shape), dX.reshape(shape), _back(dW1, w_layout), _back(dW2, w_layout), _back(dW3, w_layout))
+
+
+def mlp_act_sampled(x, w1, w2, gy, act_name, rows, cols, w3=None, w_layout="math"):
+    """Selected outputs of ``mlp_act_fwd_bwd`` computed one by one, for sizes
+    too large for the full oracle.
+
+    ``rows`` index tokens, ``cols`` index hidden units (0 <= c < f).  Returns
+    a dict with y[rows], dx[rows], dw1_cols = dW1[:, cols], dw2_rows =
+    dW2[cols, :] and (gated) dw3_cols = dW3[:, cols], in the math layout.
+    """
+    if act_name not in ACTS:
+        raise ValueError("activation")
+    W1, W2, W3 = _weights(w1, w2, w3, w_layout)
+    d = W1.shape[0]
+    X = _tokens(x, d)
+    G = _tokens(gy, d)
+    rows = np.asarray(rows, dtype=np.int64)
+    cols = np.asarray(cols, dtype=np.int64)
+
+    def block(Xs, Gs, c1, c2, c3):
+        # A, (U), H and the two pre-activation gradients for tokens Xs and
+        # hidden units given by the column blocks c1 (W1), c2 (W2 rows), c3 (W3)
+        A = Xs @ c1
+        dH = Gs @ c2.T
+        if c3 is None:
+            return act(act_name, A), dH * act_prime(act_name, A), None
+        U = Xs @ c3
+        return act(act_name, A) * U, dH * U * act_prime(act_name, A), dH * act(act_name, A)
+
+    H, dA, dU = block(X[rows], G[rows], W1, W2, W3)
+    out = dict(y=H @ W2, dx=dA @ W1.T + (0.0 if W3 is None else dU @ W3.T))
+    Hc, dAc, dUc = block(X, G, W1[:, cols], W2[cols, :], None if W3 is None else W3[:, cols])
+    out["dw1_cols"] = X.T @ dAc
+    out["dw2_rows"] = Hc.T @ G
+    if W3 is not None:
+        out["dw3_cols"] = X.T @ dUc
+    return out

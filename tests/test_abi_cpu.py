@@ -142,3 +142,33 @@ def test_ce_opts_workspace_and_bad_arguments(lib):
     assert f(2, 1, 3, 8, 8, ign, 0.1, p, N, p, p, N, p, 4096, N) == binding.TPR_ERR_NULLPTR
     assert f(2, 1, 3, 8, 8, ign, 0.1, p, p, p, p, N, p, 16, N) == binding.TPR_ERR_WORKSPACE
     assert f(2, 1, 3, 8, 8, ign, 0.1, p, p, p, p, N, N, 4096, N) == binding.TPR_ERR_WORKSPACE
+
+
+def test_mlp_act_workspace_and_bad_arguments(lib):
+    ws = lib.tp_mlp_act_workspace_bytes
+    T, d, f = 8192, 8192, 3584
+    assert ws(1, 1, 0, T, d, f) == lib.tp_mlp_workspace_bytes(1, 1, T, d, f)
+    assert ws(1, 1, 1, T, d, f) == 5 * T * f * 2 + 2 * T * d * 4            # gated, one rank
+    assert ws(4, 1, 1, T, d, f) == 5 * T * f * 2 + (4 + 8) * T * d * 4      # y and 2 x dx partials per rank
+    assert ws(0, 1, 1, T, d, f) == 0
+    fn = lib.tp_mlp_act_fwd_bwd
+    p = ctypes.c_void_p(16)  # never dereferenced: validation stops first
+    args = lambda act, w3, dw3: (1, 1, 0, act, 4, 8, 6, p, p, w3, p, p, p, p, p, dw3, p, p, 1 << 20, N)
+    assert fn(*args(3, N, N)) == binding.TPR_ERR_VALUE
+    assert b"activation" in lib.tprank_last_error()
+    assert fn(*args(-1, N, N)) == binding.TPR_ERR_VALUE
+    assert fn(*args(2, p, N)) == binding.TPR_ERR_NULLPTR                      # gated without dw3
+    a = list(args(2, p, p))
+    a[18] = 16
+    assert fn(*a) == binding.TPR_ERR_WORKSPACE
+
+
+def test_binding_signatures_match_the_header():
+    # Every ctypes signature has as many arguments as the header's prototype.
+    text = re.sub(r"/\*.*?\*/", "", open(HEADER).read(), flags=re.S)
+    protos = {m.group(1): m.group(2) for m in
+              re.finditer(r"^\s*(?:const\s+)?\w+\*?\s+\*?(\w+)\s*\(([^)]*)\)\s*;", text, flags=re.M | re.S)}
+    for name, (_, args) in binding._SIGS.items():
+        params = protos[name].strip()
+        n = 0 if params in ("", "void") else params.count(",") + 1
+        assert len(args) == n, (name, len(args), n)

@@ -156,3 +156,23 @@ def test_errors():
         mlp_act_fwd_bwd(x, w1, w2, gy, "silu", w3, "other")
     with pytest.raises(ValueError, match="partition"):
         tp_mlp_act_fwd_bwd(x, w1, w2, gy, 0, "silu", w3)
+
+
+@pytest.mark.parametrize("gated", [False, True])
+@pytest.mark.parametrize("layout", ["math", "torch"])
+def test_sampled_matches_full(gated, layout):
+    from oracle.mlp_act import mlp_act_sampled
+    x, w1, w2, gy, w3 = _inputs(9, 7, 11, seed=12, gated=gated, layout=layout)
+    rows, cols = np.array([0, 4, 8]), np.array([1, 5, 10])
+    for name in ACTS:
+        y, dx, dw1, dw2, dw3 = mlp_act_fwd_bwd(x, w1, w2, gy, name, w3, layout)
+        s = mlp_act_sampled(x, w1, w2, gy, name, rows, cols, w3, layout)
+        m = (lambda w: w) if layout == "math" else (lambda w: w.T)
+        np.testing.assert_allclose(s["y"], y[rows], rtol=1e-13, atol=1e-15)
+        np.testing.assert_allclose(s["dx"], dx[rows], rtol=1e-13, atol=1e-15)
+        np.testing.assert_allclose(s["dw1_cols"], m(dw1)[:, cols], rtol=1e-13, atol=1e-15)
+        np.testing.assert_allclose(s["dw2_rows"], m(dw2)[cols, :], rtol=1e-13, atol=1e-15)
+        if gated:
+            np.testing.assert_allclose(s["dw3_cols"], m(dw3)[:, cols], rtol=1e-13, atol=1e-15)
+        else:
+            assert "dw3_cols" not in s
