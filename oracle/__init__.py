@@ -24,7 +24,11 @@ it cites:
   smoothing, each checked against an unsharded full-vocabulary reference;
 * the TP lesson page's other element-wise activations and its gate / up
   column-parallel projections (``mlp_act.py``): tanh and SiLU MLPs and the
-  gated MLP, forward and backward, sharded and unsharded.
+  gated MLP, forward and backward, sharded and unsharded;
+* the TP lesson page's attention block (``attn_proj.py``): the column-parallel
+  QKV projection split by heads (grouped-query heads included) and the
+  row-parallel output projection, around an attention core that is not
+  part of this.
 
 Where a method reaches a result that has a plain definition (the unsharded
 product, the unsharded MLP, the unsharded cross-entropy), the oracle used for
@@ -42,6 +46,7 @@ from .mlp import gelu, gelu_prime, to_math_layout, mlp_fwd_bwd, tp_mlp_fwd_bwd, 
 from .ce import cross_entropy, vocab_parallel_ce
 from .head import head_ce, vocab_parallel_head_ce
 from .ce_options import cross_entropy_opts, vocab_parallel_ce_opts
+from .attn_proj import attn_proj_fwd_bwd, check_heads, fuse_qkv, split_qkv, tp_attn_proj_fwd_bwd
 from .mlp_act import ACTS, act, act_prime, mlp_act_fwd_bwd, mlp_act_sampled, tp_mlp_act_fwd_bwd
 
 __all__ = [
@@ -51,5 +56,6 @@ __all__ = [
     "cross_entropy", "vocab_parallel_ce",
     "head_ce", "vocab_parallel_head_ce",
     "cross_entropy_opts", "vocab_parallel_ce_opts",
+    "attn_proj_fwd_bwd", "check_heads", "fuse_qkv", "split_qkv", "tp_attn_proj_fwd_bwd",
     "ACTS", "act", "act_prime", "mlp_act_fwd_bwd", "mlp_act_sampled", "tp_mlp_act_fwd_bwd",
 ]
