@@ -39,6 +39,7 @@ INNER = dict(M=8192, K=1024, N=8192)
 CE = dict(T=4096, V=128256, parts=8)
 HEAD = dict(T=4096, d=4096, V=128256, parts=8)
 MLP_8B = dict(T=4096, d=4096, f=1792)
+ATTN = dict(T=8192, d=8192, n_q_heads=8, n_kv_heads=1, head_dim=128)
 GATED = dict(T=8192, d=8192, f=3584, act="silu")
 CE_OPTS = dict(T=4096, V=128256, v_valid=128000, parts=8, label_smoothing=0.1, ignore_frac=0.125)
 
@@ -224,6 +225,45 @@ def bench_gated_mlp(tpr, dev, steps):
             "pct_of_bf16_peak": round(100.0 * tflops / PEAK_BF16_TFLOPS, 2), "flop_per_call": flop}
 
 
+def bench_attn_proj(tpr, dev, steps):
+    """The attention-block projections of a Llama-3-70B rank at TP = 8 (8
+    query heads and 1 KV head of 128, d = 8192, T = 8192 tokens, bf16): the
+    fused QKV projection and the output projection, forward and backward,
+    one grouped launch of six GEMMs (6*T*d*(nqkv + nq) FLOP)."""
+    import torch
+
+    a = ATTN
+    T, d, dh = a["T"], a["d"], a["head_dim"]
+    nq, nkv = a["n_q_heads"] * dh, a["n_kv_heads"] * dh
+    nqkv = nq + 2 * nkv
+    g = torch.Generator(device=dev)
+    g.manual_seed(13)
+    mk = lambda shape, std: (torch.randn(shape, generator=g, device=dev) * std).bfloat16()
+    x, gy, ctx, dqkv = mk((T, d), 1.0), mk((T, d), 1.0), mk((T, nq), 1.0), mk((T, nqkv), 1.0)
+    w_qkv, w_o = mk((d, nqkv), 0.02), mk((nq, d), 0.02)
+    out = (torch.empty(T, nqkv, dtype=torch.bfloat16, device=dev), torch.empty(T, d, device=dev),
+           torch.empty(T, nq, dtype=torch.bfloat16, device=dev), torch.empty(T, d, device=dev),
+           torch.empty(d, nqkv, device=dev), torch.empty(nq, d, device=dev))
+    call = lambda: tpr.tp_attn_proj_fwd_bwd(1, x, w_qkv, w_o, ctx, gy, dqkv, a["n_q_heads"], a["n_kv_heads"], dh,
+                                            out=out)
+    for _ in range(2):
+        call()
+    torch.cuda.synchronize()
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(steps)]
+    for e in ev:
+        e[0].record()
+        call()
+        e[1].record()
+    torch.cuda.synchronize()
+    ms = sorted(e[0].elapsed_time(e[1]) for e in ev)
+    flop = 6.0 * T * d * (nqkv + nq)
+    mean = sum(ms) / len(ms)
+    tflops = flop / (mean * 1e-3) / 1e12
+    return {"config": dict(a, dtype="bf16", w_layout="math", tp_simulated=1), "steps": steps, "ms": round(mean, 4),
+            "ms_min": round(ms[0], 4), "tflops": round(tflops, 1),
+            "pct_of_bf16_peak": round(100.0 * tflops / PEAK_BF16_TFLOPS, 2), "flop_per_call": flop}
+
+
 def bench_ce_opts(tpr, workloads, dev, steps):
     """The cross-entropy with options: a 128000-entry vocabulary padded to
     128256 columns, 8 shards, label smoothing 0.1, about one position in
@@ -273,6 +313,8 @@ def main():
                     help="timed calls of the cross-entropy with options (reported beside the step; 0 = skip)")
     ap.add_argument("--gated-steps", type=int, default=5,
                     help="timed calls of the gated SiLU MLP at the 70B rank size (reported beside the step; 0 = skip)")
+    ap.add_argument("--attn-steps", type=int, default=10,
+                    help="timed calls of the 70B-rank attention projections (reported beside the step; 0 = skip)")
     ap.add_argument("--traffic-from", nargs=3, metavar=("FETCH_CSV", "WRITE_CSV", "COPY_BYTES"))
     ap.add_argument("--copy-bytes", type=int, default=0,
                     help="also run one plain copy kernel (torch.neg on fp32) of this many bytes before timing, "
@@ -366,6 +408,9 @@ def main():
     mlp_8b = None
     if args.mlp_8b_steps > 0:
         mlp_8b = bench_mlp_8b(tpr, workloads, dev, args.mlp_8b_steps)
+    attn = None
+    if args.attn_steps > 0:
+        attn = bench_attn_proj(tpr, dev, args.attn_steps)
     gated = None
     if args.gated_steps > 0:
         gated = bench_gated_mlp(tpr, dev, args.gated_steps)
@@ -439,6 +484,8 @@ def main():
         line["vocab_ce_opts"] = ce_opts
     if gated is not None:
         line["gated_silu_mlp_70b_rank"] = gated
+    if attn is not None:
+        line["attn_proj_70b_rank"] = attn
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline()
     print(json.dumps(line), flush=True)

@@ -184,6 +184,47 @@ int tp_mlp_act_fwd_bwd(int tp, int dtype, int w_layout, int act, int64_t T, int6
                        float* y, float* dx, float* dw1, float* dw3, float* dw2,
                        void* ws, size_t ws_bytes, void* stream);
 
+/* ---- attention-block projections -------------------------------------- */
+/*
+ * Bytes of workspace tp_attn_proj_fwd_bwd() needs: when tp > 1, the tp
+ * full-shape fp32 partials of y and of dx (T x d each); 0 for tp == 1 and
+ * for invalid arguments.
+ */
+size_t tp_attn_proj_workspace_bytes(int tp, int dtype, int64_t T, int64_t d, int n_q_heads, int n_kv_heads,
+                                    int head_dim);
+
+/*
+ * [TP] 2.B (figure 6-2) and section 3's head-count constraints: the QKV
+ * projection is column-parallel by heads, the output projection
+ * row-parallel; the attention core between them is not computed here (its
+ * forward output ctx and its input gradient dqkv are inputs).  With
+ * nq = n_q_heads * head_dim and nkv = n_kv_heads * head_dim (grouped-query
+ * attention when n_kv_heads < n_q_heads), rank r of `tp` owns
+ * n_q_heads / tp query heads and n_kv_heads / tp KV heads:
+ *   forward:  qkv_r = x W_qkv,r  (its column block of the fused projection),
+ *             y = sum_r ctx_r W_o,r  (ctx_r: its heads' context columns,
+ *             W_o,r: the matching rows of W_o);
+ *   backward: dW_qkv,r = x^T dqkv_r;  dx = sum_r dqkv_r W_qkv,r^T;
+ *             dctx_r = gy W_o,r^T;  dW_o,r = ctx_r^T gy;
+ * y and dx summed in rank order (the block's one reduction each way).
+ * Fused QKV column order: one contiguous block of (nq + 2 nkv) / tp columns
+ * per rank, holding that rank's query heads, then its K heads, then its V
+ * heads (head_dim columns per head); qkv and dqkv use the same order, ctx
+ * and dctx the plain head order (nq columns).
+ *   x, gy: T x d;  ctx: T x nq;  dqkv: T x (nq + 2 nkv), all in `dtype`;
+ *   w_qkv: d x (nq + 2 nkv) for TPR_W_MATH or its transpose for
+ *   TPR_W_TORCH;  w_o: nq x d (math) or d x nq (torch), in `dtype`;
+ *   qkv: T x (nq + 2 nkv) and dctx: T x nq in `dtype` (the core's operands);
+ *   y, dx: fp32 T x d;  dw_qkv, dw_o: fp32 like w_qkv, w_o.
+ * Errors: SHAPE (n_q_heads not a multiple of n_kv_heads, head_dim < 1),
+ * PARTITION (tp < 1, or tp not dividing both head counts: KV heads are not
+ * replicated), DTYPE, NULLPTR, WORKSPACE, HIP.
+ */
+int tp_attn_proj_fwd_bwd(int tp, int dtype, int w_layout, int64_t T, int64_t d, int n_q_heads, int n_kv_heads,
+                         int head_dim, const void* x, const void* w_qkv, const void* w_o, const void* ctx,
+                         const void* gy, const void* dqkv, void* qkv, float* y, void* dctx, float* dx,
+                         float* dw_qkv, float* dw_o, void* ws, size_t ws_bytes, void* stream);
+
 /* ---- vocabulary-parallel cross-entropy -------------------------------- */
 /*
  * Bytes of workspace vocab_parallel_ce_fwd_bwd() needs (the T per-row

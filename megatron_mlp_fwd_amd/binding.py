@@ -34,6 +34,8 @@ _SIGS = {
     "tp_mlp_fwd_bwd": (_i32, [_i32, _i32, _i32, _i64, _i64, _i64, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
     "tp_mlp_act_workspace_bytes": (_sz, [_i32, _i32, _i32, _i64, _i64, _i64]),
     "tp_mlp_act_fwd_bwd": (_i32, [_i32, _i32, _i32, _i32, _i64, _i64, _i64] + [_vp] * 11 + [_sz, _vp]),
+    "tp_attn_proj_workspace_bytes": (_sz, [_i32, _i32, _i64, _i64, _i32, _i32, _i32]),
+    "tp_attn_proj_fwd_bwd": (_i32, [_i32, _i32, _i32, _i64, _i64, _i32, _i32, _i32] + [_vp] * 13 + [_sz, _vp]),
     "vocab_parallel_ce_workspace_bytes": (_sz, [_i32, _i64, _i64]),
     "vocab_parallel_ce_fwd_bwd": (_i32, [_i32, _i32, _i64, _i64, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
     "vocab_parallel_ce_opts_workspace_bytes": (_sz, [_i32, _i64, _i64]),
@@ -244,6 +246,56 @@ def tp_mlp_act_fwd_bwd(tp, x, w1, w2, gy, act="gelu", w3=None, w_layout="math", 
                                       _ptr(w2), _ptr(gy), _ptr(y), _ptr(dx), _ptr(dw1), _ptr(dw3), _ptr(dw2),
                                       _ptr(ws), wsb, _stream(stream)))
     return y, dx, dw1, dw2, dw3
+
+
+def tp_attn_proj_workspace_bytes(tp, dtype, T, d, n_q_heads, n_kv_heads, head_dim):
+    return load_library().tp_attn_proj_workspace_bytes(tp, DTYPES[dtype], T, d, n_q_heads, n_kv_heads, head_dim)
+
+
+def tp_attn_proj_fwd_bwd(tp, x, w_qkv, w_o, ctx, gy, dqkv, n_q_heads, n_kv_heads, head_dim, w_layout="math",
+                         out=None, workspace=None, stream=None):
+    """Attention-block projections over ``tp`` simulated ranks: the fused
+    QKV projection (rank-major column blocks of query, K and V heads) and
+    the output projection, forward and backward, around an attention core
+    whose context ``ctx`` and input gradient ``dqkv`` are given.  Returns
+    (qkv, y, dctx, dx, dw_qkv, dw_o): qkv and dctx in the input dtype, the
+    rest fp32."""
+    lib = load_library()
+    layout = W_LAYOUTS[w_layout]
+    dt = x.dtype
+    if dt not in DTYPES:
+        raise ValueError(f"unsupported dtype {dt}")
+    if x.dim() != 2:
+        raise ValueError("x must be 2-D (tokens x d)")
+    T, d = x.shape
+    nq, nkv = n_q_heads * head_dim, n_kv_heads * head_dim
+    nqkv = nq + 2 * nkv
+    wqs, wos = ((d, nqkv), (nq, d)) if layout == 0 else ((nqkv, d), (d, nq))
+    dev = x.device
+    _need(x, "x", (T, d), dt, dev)
+    _need(gy, "gy", (T, d), dt, dev)
+    _need(w_qkv, "w_qkv", wqs, dt, dev)
+    _need(w_o, "w_o", wos, dt, dev)
+    _need(ctx, "ctx", (T, nq), dt, dev)
+    _need(dqkv, "dqkv", (T, nqkv), dt, dev)
+    if out is None:
+        out = (torch.empty(T, nqkv, dtype=dt, device=dev), torch.empty(T, d, device=dev),
+               torch.empty(T, nq, dtype=dt, device=dev), torch.empty(T, d, device=dev),
+               torch.empty(wqs, device=dev), torch.empty(wos, device=dev))
+    qkv, y, dctx, dx, dwq, dwo = out
+    _need(qkv, "qkv", (T, nqkv), dt, dev)
+    _need(y, "y", (T, d), torch.float32, dev)
+    _need(dctx, "dctx", (T, nq), dt, dev)
+    _need(dx, "dx", (T, d), torch.float32, dev)
+    _need(dwq, "dw_qkv", wqs, torch.float32, dev)
+    _need(dwo, "dw_o", wos, torch.float32, dev)
+    ws, wsb = _workspace(lib.tp_attn_proj_workspace_bytes(tp, DTYPES[dt], T, d, n_q_heads, n_kv_heads, head_dim),
+                         dev, workspace)
+    with torch.cuda.device(dev):
+        _check(lib.tp_attn_proj_fwd_bwd(tp, DTYPES[dt], layout, T, d, n_q_heads, n_kv_heads, head_dim, _ptr(x),
+                                        _ptr(w_qkv), _ptr(w_o), _ptr(ctx), _ptr(gy), _ptr(dqkv), _ptr(qkv), _ptr(y),
+                                        _ptr(dctx), _ptr(dx), _ptr(dwq), _ptr(dwo), _ptr(ws), wsb, _stream(stream)))
+    return qkv, y, dctx, dx, dwq, dwo
 
 
 def vocab_parallel_ce_workspace_bytes(parts, T, V):

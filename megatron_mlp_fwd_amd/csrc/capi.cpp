@@ -419,6 +419,80 @@ int tp_mlp_act_fwd_bwd(int tp, int dtype, int w_layout, int act, int64_t T, int6
                      stream);
 }
 
+// ---------------------------------------------------------------- attention projections
+size_t tp_attn_proj_workspace_bytes(int tp, int dtype, int64_t T, int64_t d, int n_q_heads, int n_kv_heads,
+                                    int head_dim) {
+  if (tp < 1 || !dtype_ok(dtype) || T < 0 || d < 0 || n_q_heads < 1 || n_kv_heads < 1 || head_dim < 1) return 0;
+  return tp > 1 ? 2 * (size_t)tp * align256((size_t)(T * d * 4)) : 0;  // y and dx partials
+}
+
+int tp_attn_proj_fwd_bwd(int tp, int dtype, int w_layout, int64_t T, int64_t d, int n_q_heads, int n_kv_heads,
+                         int head_dim, const void* x, const void* w_qkv, const void* w_o, const void* ctx,
+                         const void* gy, const void* dqkv, void* qkv, float* y, void* dctx, float* dx, float* dw_qkv,
+                         float* dw_o, void* ws, size_t ws_bytes, void* stream) {
+  if (!dim_ok(T) || !dim_ok(d) || head_dim < 1)
+    return fail(TPR_ERR_SHAPE, "T, d must be in [0, 2^31) and head_dim >= 1 (got %lld, %lld, %d)", (long long)T,
+                (long long)d, head_dim);
+  if (n_q_heads < 1 || n_kv_heads < 1 || n_q_heads % n_kv_heads != 0)
+    return fail(TPR_ERR_SHAPE, "query heads (%d) must be a positive multiple of KV heads (%d)", n_q_heads,
+                n_kv_heads);
+  if (tp < 1) return fail(TPR_ERR_PARTITION, "tp must be >= 1 (got %d)", tp);
+  if (n_q_heads % tp != 0 || n_kv_heads % tp != 0)
+    return fail(TPR_ERR_PARTITION, "tp = %d must divide the query heads (%d) and the KV heads (%d)", tp, n_q_heads,
+                n_kv_heads);
+  if (!dtype_ok(dtype)) return fail(TPR_ERR_DTYPE, "unknown dtype %d", dtype);
+  if (w_layout != TPR_W_MATH && w_layout != TPR_W_TORCH) return fail(TPR_ERR_DTYPE, "unknown w_layout %d", w_layout);
+  const int64_t nq = (int64_t)n_q_heads * head_dim, nkv = (int64_t)n_kv_heads * head_dim;
+  const int64_t nqkv = nq + 2 * nkv;
+  if (!dim_ok(nqkv)) return fail(TPR_ERR_SHAPE, "projection width %lld out of range", (long long)nqkv);
+  if ((T * d > 0 && (x == nullptr || gy == nullptr || y == nullptr || dx == nullptr)) ||
+      (T * nqkv > 0 && (dqkv == nullptr || qkv == nullptr || ctx == nullptr || dctx == nullptr)) ||
+      (d * nqkv > 0 && (w_qkv == nullptr || w_o == nullptr || dw_qkv == nullptr || dw_o == nullptr)))
+    return fail(TPR_ERR_NULLPTR, "a non-empty input or output pointer is NULL");
+  const size_t need = tp_attn_proj_workspace_bytes(tp, dtype, T, d, n_q_heads, n_kv_heads, head_dim);
+  if (ws_bytes < need || (need > 0 && ws == nullptr))
+    return fail(TPR_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", need, ws_bytes);
+
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const int64_t e = esize(dtype);
+  const bool math = w_layout == TPR_W_MATH;
+  const bool direct = tp == 1;
+  const int64_t pstride = (int64_t)(align256((size_t)(T * d * 4)) / 4);
+  float* ypart = static_cast<float*>(ws);
+  float* xpart = direct ? nullptr : ypart + (int64_t)tp * pstride;
+  const int raw = dtype == TPR_BF16 ? tpr::EPI_BF16 : tpr::EPI_F32;  // outputs the core consumes
+  const int64_t wr = nqkv / tp, kr = nq / tp;  // rank r: QKV columns [r wr, (r+1) wr), W_O rows [r kr, (r+1) kr)
+  std::vector<Job> jobs;  // every product is independent of the others: one grouped launch
+  for (int r = 0; r < tp; ++r) {
+    const int64_t c0 = r * wr, k0 = r * kr;
+    float* ydst = direct ? y : ypart + r * pstride;
+    float* xdst = direct ? dx : xpart + r * pstride;
+    // Column-parallel QKV: qkv_r = x W_r; dW_r = x^T dqkv_r; dx_r = dqkv_r W_r^T.
+    // Row-parallel output: y_r = ctx_r W_O,r; dctx_r = gy W_O,r^T; dW_O,r = ctx_r^T gy.
+    if (math) {  // w_qkv d x nqkv, w_o nq x d
+      jobs.push_back(job(prob(x, d, 1, cb(w_qkv) + c0 * e, nqkv, 1, static_cast<char*>(qkv) + c0 * e, nqkv, T, wr, d), true, false, raw));
+      jobs.push_back(job(prob(x, 1, d, cb(dqkv) + c0 * e, nqkv, 1, dw_qkv + c0, nqkv, d, wr, T), false, false, tpr::EPI_F32));
+      jobs.push_back(job(prob(cb(dqkv) + c0 * e, nqkv, 1, cb(w_qkv) + c0 * e, 1, nqkv, xdst, d, T, d, wr), true, true, tpr::EPI_F32));
+      jobs.push_back(job(prob(cb(ctx) + k0 * e, nq, 1, cb(w_o) + k0 * d * e, d, 1, ydst, d, T, d, kr), true, false, tpr::EPI_F32));
+      jobs.push_back(job(prob(gy, d, 1, cb(w_o) + k0 * d * e, 1, d, static_cast<char*>(dctx) + k0 * e, nq, T, kr, d), true, true, raw));
+      jobs.push_back(job(prob(cb(ctx) + k0 * e, 1, nq, gy, d, 1, dw_o + k0 * d, d, kr, d, T), false, false, tpr::EPI_F32));
+    } else {  // w_qkv (nqkv, d), w_o (d, nq)
+      jobs.push_back(job(prob(x, d, 1, cb(w_qkv) + c0 * d * e, 1, d, static_cast<char*>(qkv) + c0 * e, nqkv, T, wr, d), true, true, raw));
+      jobs.push_back(job(prob(cb(dqkv) + c0 * e, 1, nqkv, x, d, 1, dw_qkv + c0 * d, d, wr, d, T), false, false, tpr::EPI_F32));
+      jobs.push_back(job(prob(cb(dqkv) + c0 * e, nqkv, 1, cb(w_qkv) + c0 * d * e, d, 1, xdst, d, T, d, wr), true, false, tpr::EPI_F32));
+      jobs.push_back(job(prob(cb(ctx) + k0 * e, nq, 1, cb(w_o) + k0 * e, 1, nq, ydst, d, T, d, kr), true, true, tpr::EPI_F32));
+      jobs.push_back(job(prob(gy, d, 1, cb(w_o) + k0 * e, nq, 1, static_cast<char*>(dctx) + k0 * e, nq, T, kr, d), true, false, raw));
+      jobs.push_back(job(prob(gy, 1, d, cb(ctx) + k0 * e, nq, 1, dw_o + k0, nq, d, kr, T), false, false, tpr::EPI_F32));
+    }
+  }
+  hipError_t he;
+  if ((he = run_jobs(jobs, dtype, s)) != hipSuccess) return hip_fail(he, "projection GEMMs");
+  // The block's one reduction each way: y = sum_r y_r, dx = sum_r dx_r.
+  if ((he = finish_sum(y, T, d, ypart, tp, pstride, direct, s)) != hipSuccess) return hip_fail(he, "y reduction");
+  if ((he = finish_sum(dx, T, d, xpart, tp, pstride, direct, s)) != hipSuccess) return hip_fail(he, "dx reduction");
+  return TPR_OK;
+}
+
 // ---------------------------------------------------------------- vocab CE
 size_t vocab_parallel_ce_workspace_bytes(int parts, int64_t T, int64_t V) {
   if (parts < 1 || T < 0 || V < 0) return 0;

@@ -172,3 +172,23 @@ def test_binding_signatures_match_the_header():
         params = protos[name].strip()
         n = 0 if params in ("", "void") else params.count(",") + 1
         assert len(args) == n, (name, len(args), n)
+
+
+def test_attn_proj_workspace_and_bad_arguments(lib):
+    ws = lib.tp_attn_proj_workspace_bytes
+    assert ws(1, 1, 8192, 8192, 8, 1, 128) == 0
+    assert ws(8, 1, 4096, 4096, 32, 8, 128) == 2 * 8 * 4096 * 4096 * 4
+    assert ws(8, 1, 4096, 4096, 32, 8, 0) == 0
+    f = lib.tp_attn_proj_fwd_bwd
+    p = ctypes.c_void_p(16)  # never dereferenced: validation stops first
+    call = lambda tp, hq, hkv, dh, dtype=1, layout=0, wsb=1 << 30: f(tp, dtype, layout, 4, 8, hq, hkv, dh,
+                                                                      *[p] * 12, p, wsb, N)
+    assert call(16, 32, 8, 4) == binding.TPR_ERR_PARTITION      # KV heads not divisible (no replication)
+    assert b"KV heads" in lib.tprank_last_error()
+    assert call(3, 32, 8, 4) == binding.TPR_ERR_PARTITION
+    assert call(0, 32, 8, 4) == binding.TPR_ERR_PARTITION
+    assert call(2, 12, 8, 4) == binding.TPR_ERR_SHAPE           # query heads not a multiple of KV heads
+    assert call(2, 8, 8, 0) == binding.TPR_ERR_SHAPE
+    assert call(2, 8, 8, 4, dtype=5) == binding.TPR_ERR_DTYPE
+    assert call(2, 8, 8, 4, layout=2) == binding.TPR_ERR_DTYPE
+    assert call(2, 8, 8, 4, wsb=16) == binding.TPR_ERR_WORKSPACE
