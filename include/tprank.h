@@ -118,7 +118,9 @@ int sharded_matmul_fwd_bwd(int axis, int parts, int dtype, int64_t M, int64_t K,
  * Bytes of workspace tp_mlp_fwd_bwd() needs: gelu' of the pre-activation
  * and the activation (T x f each, in `dtype`; the first buffer is reused for
  * the gradient at the pre-activation), plus, when tp > 1, the tp full-shape
- * fp32 partials of y and of dx.  Returns 0 for invalid arguments.
+ * fp32 partials of y and of dx, plus (TPR_BF16, when gy W2^T fits in the
+ * idle compute units of the forward launch's last round) that product in
+ * fp32 (T x f).  Returns 0 for invalid arguments.
  */
 size_t tp_mlp_workspace_bytes(int tp, int dtype, int64_t T, int64_t d, int64_t f);
 
@@ -132,7 +134,11 @@ size_t tp_mlp_workspace_bytes(int tp, int dtype, int64_t T, int64_t d, int64_t f
  *             dW2_r = H_r^T gy;  dZ_r = (gy W2_r^T) * gelu'(P_r) (fused);
  *             dW1_r = x^T dZ_r;  dx_r = dZ_r W1_r^T;
  * then y = sum_r Z_r and dx = sum_r dx_r (the MLP's one reduction each way,
- * fixed rank order).  With tp == 1 the call computes one rank's share: pass
+ * fixed rank order).  For TPR_BF16, when the forward launch leaves enough
+ * compute units idle, gy W2_r^T is computed alongside P_r (it does not
+ * depend on it), kept in fp32 and multiplied by gelu'(P_r) afterwards (one
+ * rounding, as in the fused epilogue otherwise used).  With tp == 1 the call
+ * computes one rank's share: pass
  * the rank's weight shards (w1 d x f_r, w2 f_r x d in TPR_W_MATH) and y, dx
  * are that rank's partials Z_r, dx_r.  For TPR_BF16 the activation and the
  * pre-activation gradient are rounded to bf16 (they are GEMM operands), and

@@ -229,10 +229,37 @@ int sharded_matmul_fwd_bwd(int axis, int parts, int dtype, int64_t M, int64_t K,
 // ---------------------------------------------------------------- TP MLP
 namespace {
 
+constexpr int kCUs = 256;    // compute units of an MI355X
+constexpr int kTile = 256;   // block tile of the bf16 GEMM
+
+// Rows of dH = gy W2^T computed in the fc1 launch of the plain bf16 MLP: T
+// (all of it) or 0.  fc1 fills sum_r ceil(T/256) ceil(f_r/256) tiles of
+// K = d; when its last round leaves enough compute units idle for every dH
+// tile (same K), dH runs there instead of in the next launch.  Moving only
+// some leading row blocks measured no gain (the fc1 launch grew by what the
+// next one lost, plus the separate multiply).  GELU only: the kernel
+// instance for other activations takes activation epilogues alone.
+int64_t cosched_rows(int dtype, int act, int tp, int64_t T, int64_t f) {
+  if (dtype != TPR_BF16 || act != TPR_ACT_GELU || T <= 0) return 0;
+  const int64_t tiles_m = (T + kTile - 1) / kTile;
+  int64_t n1 = 0, nb = 0;
+  for (int r = 0; r < tp; ++r) {
+    int64_t lo, hi;
+    shard_of(f, tp, r, &lo, &hi);
+    const int64_t tn = (hi - lo + kTile - 1) / kTile;
+    n1 += tiles_m * tn;
+    nb += tn;
+  }
+  if (nb == 0) return 0;
+  const int64_t free = (kCUs - n1 % kCUs) % kCUs;
+  return (free / nb) * kTile >= T ? T : 0;
+}
+
 size_t mlp_workspace(int tp, int dtype, bool gated, int64_t T, int64_t d, int64_t f) {
   if (tp < 1 || !dtype_ok(dtype) || T < 0 || d < 0 || f < 0) return 0;
   const size_t tf = align256((size_t)(T * f * esize(dtype))), td = align256((size_t)(T * d * 4));
-  if (!gated) return 2 * tf + (tp > 1 ? 2 * (size_t)tp * td : 0);
+  if (!gated)  // sigma'(P) / dZ, H, partials, fp32 dH of the co-scheduled rows
+    return 2 * tf + (tp > 1 ? 2 * (size_t)tp * td : 0) + align256((size_t)(cosched_rows(dtype, TPR_ACT_GELU, tp, T, f) * f * 4));
   // gate, up, H, dA (dH first), dU; y partials when tp > 1; two dx partials per rank
   return 5 * tf + (tp > 1 ? (size_t)tp * td : 0) + 2 * (size_t)tp * td;
 }
@@ -256,9 +283,18 @@ int mlp_plain(int tp, int dtype, bool math, int act, int64_t T, int64_t d, int64
   const int64_t pstride = (int64_t)(align256((size_t)(T * d * 4)) / 4);
   float* zpart = reinterpret_cast<float*>(wsb + 2 * align256((size_t)(T * f * e)));
   float* xpart = zpart + (int64_t)tp * pstride;
+  const int64_t T1 = cosched_rows(dtype, act, tp, T, f);  // dH rows [0, T1) join the fc1 launch
+  float* dh1 = reinterpret_cast<float*>(wsb + 2 * align256((size_t)(T * f * e)) +
+                                        (tp > 1 ? 2 * (size_t)tp * align256((size_t)(T * d * 4)) : 0));
   const bool direct = tp == 1;
   int nslots = 0;
-  std::vector<Job> fwd1, mid, last;  // launch groups: fc1 | fc2, dW2, dH | dW1, dx
+  std::vector<Job> fwd1, mid, last;  // launch groups: fc1 (+ dH rows < T1) | fc2, dW2, dH | dW1, dx
+  struct Scale {
+    char* pre;        // sigma'(P) of rows < T1, becomes dZ
+    const float* dh;  // their fp32 dH
+    int64_t n;        // T1 * f_r elements
+  };
+  std::vector<Scale> scale;
   for (int r = 0; r < tp; ++r) {
     int64_t lo, hi;
     shard_of(f, tp, r, &lo, &hi);
@@ -275,7 +311,12 @@ int mlp_plain(int tp, int dtype, bool math, int act, int64_t T, int64_t d, int64
       fwd1.push_back(job(p1, true, false, tpr::EPI_ACT));
       mid.push_back(job(prob(Hr, fr, 1, cb(w2) + lo * d * e, d, 1, ydst, d, T, d, fr), true, false, tpr::EPI_F32));
       mid.push_back(job(prob(Hr, 1, fr, gy, d, 1, dw2 + lo * d, d, fr, d, T), false, false, tpr::EPI_F32));
-      mid.push_back(job(prob(gy, d, 1, cb(w2) + lo * d * e, 1, d, Pr, fr, T, fr, d, Pr), true, true, tpr::EPI_MUL));
+      if (T1 > 0)
+        fwd1.push_back(job(prob(gy, d, 1, cb(w2) + lo * d * e, 1, d, dh1 + T1 * lo, fr, T1, fr, d), true, true,
+                           tpr::EPI_F32));
+      if (T1 < T)
+        mid.push_back(job(prob(cb(gy) + T1 * d * e, d, 1, cb(w2) + lo * d * e, 1, d, Pr + T1 * fr * e, fr, T - T1, fr,
+                               d, Pr + T1 * fr * e), true, true, tpr::EPI_MUL));
       last.push_back(job(prob(x, 1, d, Pr, fr, 1, dw1 + lo, f, d, fr, T), false, false, tpr::EPI_F32));
       last.push_back(job(prob(Pr, fr, 1, cb(w1) + lo * e, 1, f, xdst, d, T, d, fr), true, true, tpr::EPI_F32));
     } else {  // w1 (f, d), w2 (d, f)
@@ -284,14 +325,27 @@ int mlp_plain(int tp, int dtype, bool math, int act, int64_t T, int64_t d, int64
       fwd1.push_back(job(p1, true, true, tpr::EPI_ACT));
       mid.push_back(job(prob(Hr, fr, 1, cb(w2) + lo * e, 1, f, ydst, d, T, d, fr), true, true, tpr::EPI_F32));
       mid.push_back(job(prob(gy, 1, d, Hr, fr, 1, dw2 + lo, f, d, fr, T), false, false, tpr::EPI_F32));
-      mid.push_back(job(prob(gy, d, 1, cb(w2) + lo * e, f, 1, Pr, fr, T, fr, d, Pr), true, false, tpr::EPI_MUL));
+      if (T1 > 0)
+        fwd1.push_back(job(prob(gy, d, 1, cb(w2) + lo * e, f, 1, dh1 + T1 * lo, fr, T1, fr, d), true, false,
+                           tpr::EPI_F32));
+      if (T1 < T)
+        mid.push_back(job(prob(cb(gy) + T1 * d * e, d, 1, cb(w2) + lo * e, f, 1, Pr + T1 * fr * e, fr, T - T1, fr, d,
+                               Pr + T1 * fr * e), true, false, tpr::EPI_MUL));
       last.push_back(job(prob(Pr, 1, fr, x, d, 1, dw1 + lo * d, d, fr, d, T), false, false, tpr::EPI_F32));
       last.push_back(job(prob(Pr, fr, 1, cb(w1) + lo * d * e, d, 1, xdst, d, T, d, fr), true, false, tpr::EPI_F32));
     }
+    if (T1 > 0 && T1 < T) scale.push_back(Scale{Pr, dh1 + T1 * lo, T1 * fr});
     ++nslots;
   }
   hipError_t he;
   if ((he = run_jobs(fwd1, dtype, s)) != hipSuccess) return hip_fail(he, "fc1 GEMM");
+  // dZ = dH * sigma'(P) for the rows whose dH ran with fc1 (fr columns each;
+  // the first T1 rows of a rank's block are its first T1 fr elements, and
+  // with T1 == T the ranks' blocks tile both buffers whole).
+  if (T1 == T && T > 0) scale.push_back(Scale{pre, dh1, T * f});
+  for (const Scale& c : scale)
+    if ((he = tpr::launch_mul_f32_into(dtype, c.pre, c.dh, c.n, s)) != hipSuccess)
+      return hip_fail(he, "dZ of the co-scheduled rows");
   if ((he = run_jobs(mid, dtype, s)) != hipSuccess) return hip_fail(he, "fc2 / dW2 / dH GEMMs");
   if ((he = run_jobs(last, dtype, s)) != hipSuccess) return hip_fail(he, "dW1 / dx GEMMs");
   // The block's one reduction each way: y = sum_r Z_r, dx = sum_r dx_r.

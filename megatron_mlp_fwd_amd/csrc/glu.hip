@@ -138,6 +138,40 @@ __global__ __launch_bounds__(256) void glu_bwd_f32(float* __restrict__ dA, const
   }
 }
 
+// dst = bf16(dst * src), src fp32: the gradient at the pre-activation for
+// rows whose dH (fp32) was computed apart from the sigma'(P) it multiplies.
+__global__ __launch_bounds__(256) void mul_f32_into_bf16(uint16_t* __restrict__ dst, const float* __restrict__ src,
+                                                         int64_t n) {
+  const int64_t nv = n / 8;
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < nv; i += stride) {
+    const u32x4 p = reinterpret_cast<const u32x4*>(dst)[i];
+    const f32x4 a = reinterpret_cast<const f32x4*>(src)[2 * i];
+    const f32x4 b = reinterpret_cast<const f32x4*>(src)[2 * i + 1];
+    u32x4 o;
+    o[0] = pack2(a[0] * bf_lo(p[0]), a[1] * bf_hi(p[0]));
+    o[1] = pack2(a[2] * bf_lo(p[1]), a[3] * bf_hi(p[1]));
+    o[2] = pack2(b[0] * bf_lo(p[2]), b[1] * bf_hi(p[2]));
+    o[3] = pack2(b[2] * bf_lo(p[3]), b[3] * bf_hi(p[3]));
+    reinterpret_cast<u32x4*>(dst)[i] = o;
+  }
+  const int64_t t = 8 * nv + blockIdx.x * (int64_t)blockDim.x + threadIdx.x;
+  if (t < n) dst[t] = to_bf(src[t] * bf(dst[t]));
+}
+
+__global__ __launch_bounds__(256) void mul_f32_into_bf16_scalar(uint16_t* __restrict__ dst,
+                                                                const float* __restrict__ src, int64_t n) {
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < n; i += stride)
+    dst[i] = to_bf(src[i] * bf(dst[i]));
+}
+
+__global__ __launch_bounds__(256) void mul_f32_into_f32(float* __restrict__ dst, const float* __restrict__ src,
+                                                        int64_t n) {
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < n; i += stride) dst[i] *= src[i];
+}
+
 unsigned grid_for(int64_t nvec) {
   const int64_t b = (nvec + 255) / 256;
   return (unsigned)(b < 1 ? 1 : (b > 4096 ? 4096 : b));
@@ -167,6 +201,19 @@ hipError_t launch_glu_bwd(int dtype, void* dA, const void* A, const void* U, voi
   else
     hipLaunchKernelGGL(glu_bwd_f32, dim3(grid_for(n / 4)), dim3(256), 0, s, static_cast<float*>(dA),
                        static_cast<const float*>(A), static_cast<const float*>(U), static_cast<float*>(dU), n, act);
+  return hipGetLastError();
+}
+
+hipError_t launch_mul_f32_into(int dtype, void* dst, const float* src, int64_t n, hipStream_t s) {
+  if (n <= 0) return hipSuccess;
+  const bool vec = reinterpret_cast<uintptr_t>(dst) % 16 == 0 && reinterpret_cast<uintptr_t>(src) % 16 == 0;
+  if (dtype == 1 && vec)
+    hipLaunchKernelGGL(mul_f32_into_bf16, dim3(grid_for(n / 8)), dim3(256), 0, s, static_cast<uint16_t*>(dst), src, n);
+  else if (dtype == 1)
+    hipLaunchKernelGGL(mul_f32_into_bf16_scalar, dim3(grid_for(n)), dim3(256), 0, s, static_cast<uint16_t*>(dst), src,
+                       n);
+  else
+    hipLaunchKernelGGL(mul_f32_into_f32, dim3(grid_for(n)), dim3(256), 0, s, static_cast<float*>(dst), src, n);
   return hipGetLastError();
 }
 
