@@ -225,6 +225,48 @@ def bench_gated_mlp(tpr, dev, steps):
             "pct_of_bf16_peak": round(100.0 * tflops / PEAK_BF16_TFLOPS, 2), "flop_per_call": flop}
 
 
+def _time_calls(call, runs, warmup=5):
+    """Median and minimum (µs) of `runs` calls, each bracketed by HIP events
+    on the current stream, after `warmup` untimed calls."""
+    import torch
+
+    for _ in range(warmup):
+        call()
+    torch.cuda.synchronize()
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(runs)]
+    for e in ev:
+        e[0].record()
+        call()
+        e[1].record()
+    torch.cuda.synchronize()
+    us = sorted(1e3 * e[0].elapsed_time(e[1]) for e in ev)
+    return {"median_us": round(us[len(us) // 2], 2), "min_us": round(us[0], 2), "runs": runs}
+
+
+def bench_small_configs(tpr, workloads, dev, runs):
+    """Latency of the fp32 walk-through configurations (launch-bound: reported
+    in µs, no roofline): the 3x5x4 sharded GEMM on each axis at 2 and 7
+    parts, and the tp=4 MLP of (2, 8, 64) tokens with f=256 in the torch
+    layout; plus the vocab CE of the step timed over `runs` calls."""
+    out = {}
+    a, b, g = workloads.sharded_gemm_tiny(seed=0, device=dev)
+    for axis in ("rows", "columns", "inner"):
+        for parts in (2, 7):
+            out[f"sharded_gemm_m3k5n4_{axis}_p{parts}"] = _time_calls(
+                lambda: tpr.sharded_matmul_fwd_bwd(axis, parts, a, b, g), runs)
+    x, w1, w2, gy = workloads.tp_mlp_tiny(seed=0, device=dev)
+    out["tp_mlp_tp4_x2x8x64_f256_fp32"] = _time_calls(lambda: tpr.tp_mlp_fwd_bwd(4, x, w1, w2, gy, "torch"), runs)
+    logits, labels = workloads.vocab_ce(T=CE["T"], V=CE["V"], seed=2, device=dev)
+    import torch
+    ce_out = (torch.empty((), device=dev), torch.empty_like(logits), None)
+    ws = torch.empty(tpr.vocab_parallel_ce_workspace_bytes(CE["parts"], CE["T"], CE["V"]), dtype=torch.uint8,
+                     device=dev)
+    r = _time_calls(lambda: tpr.vocab_parallel_ce_fwd_bwd(CE["parts"], logits, labels, out=ce_out, workspace=ws), runs)
+    r["gbs_at_median"] = round(4.0 * CE["T"] * CE["V"] / (r["median_us"] * 1e-6) / 1e9, 1)
+    out["vocab_ce_t4096_v128256_p8"] = r
+    return out
+
+
 def bench_attn_proj(tpr, dev, steps):
     """The attention-block projections of a Llama-3-70B rank at TP = 8 (8
     query heads and 1 KV head of 128, d = 8192, T = 8192 tokens, bf16): the
@@ -315,6 +357,8 @@ def main():
                     help="timed calls of the gated SiLU MLP at the 70B rank size (reported beside the step; 0 = skip)")
     ap.add_argument("--attn-steps", type=int, default=10,
                     help="timed calls of the 70B-rank attention projections (reported beside the step; 0 = skip)")
+    ap.add_argument("--small-runs", type=int, default=100,
+                    help="timed calls per small (latency-bound) configuration and of the CE (0 = skip)")
     ap.add_argument("--traffic-from", nargs=3, metavar=("FETCH_CSV", "WRITE_CSV", "COPY_BYTES"))
     ap.add_argument("--copy-bytes", type=int, default=0,
                     help="also run one plain copy kernel (torch.neg on fp32) of this many bytes before timing, "
@@ -408,6 +452,9 @@ def main():
     mlp_8b = None
     if args.mlp_8b_steps > 0:
         mlp_8b = bench_mlp_8b(tpr, workloads, dev, args.mlp_8b_steps)
+    small = None
+    if args.small_runs > 0:
+        small = bench_small_configs(tpr, workloads, dev, args.small_runs)
     attn = None
     if args.attn_steps > 0:
         attn = bench_attn_proj(tpr, dev, args.attn_steps)
@@ -486,6 +533,8 @@ def main():
         line["gated_silu_mlp_70b_rank"] = gated
     if attn is not None:
         line["attn_proj_70b_rank"] = attn
+    if small is not None:
+        line["latency"] = small
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline()
     print(json.dumps(line), flush=True)
