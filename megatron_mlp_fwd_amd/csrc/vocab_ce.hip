@@ -288,6 +288,7 @@ enum { CE_PLAIN = 0, CE_OPT = 1, CE_OPT_SMOOTH = 2 };
 constexpr int CP_NT = 512;
 constexpr int CP_NW = CP_NT / 64;
 constexpr int CP_RS = 22;           // register slots per thread
+constexpr int CP_RA = 11;           // of which part A (see ce_pair_kernel)
 constexpr int CP_LDS_VEC = 4864;    // LDS capacity in 16-byte vectors (76 KB)
 constexpr uint32_t CP_OOB = 0x80000000u;
 
@@ -298,6 +299,8 @@ __global__ __launch_bounds__(CP_NT) __attribute__((amdgpu_waves_per_eu(4, 4))) v
   constexpr bool OPT = MODE != CE_PLAIN, SMOOTH = MODE == CE_OPT_SMOOTH;
   __shared__ __attribute__((aligned(1024))) u32x4 part[CP_LDS_VEC];
   __shared__ float red[CP_NW];
+  __shared__ float red_a[CP_NW];
+  __shared__ float red_b[CP_NW];
   __shared__ float red_z[CP_NW];
   __shared__ float tail_sh[8];  // the vocabulary's last rem logits, then their exp
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
@@ -329,58 +332,61 @@ __global__ __launch_bounds__(CP_NT) __attribute__((amdgpu_waves_per_eu(4, 4))) v
   const bool tail = OPT && wid == 0 && lane < rem;
   if (tail) tail_sh[lane] = __uint_as_float((uint32_t)logits[row * V + 8 * nfull + lane] << 16);
 
+  // Loads, in issue order: register slots [0, CP_RA), the LDS part, register
+  // slots [CP_RA, CP_RS).  Slot s of thread tid holds vector s * CP_NT + tid;
+  // lanes past the row end load zeros (out of range) and are skipped below.
+  // Part A (the first slots, the LDS part and the tail) is reduced and
+  // exponentiated against its own maximum m_A while part B still arrives;
+  // part B then uses the row maximum m, and part A's values are scaled by
+  // exp(m_A - m) <= 1 wherever they are used (exact up to rounding).
+  u32x4 v[CP_RS];
+#pragma unroll
+  for (int s = 0; s < CP_RA; ++s) {
+    const int i = s * CP_NT + tid;
+    v[s] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                                         rz, i < nreg ? (uint32_t)(16 * i) : CP_OOB, 0, 2));
+  }
+  asm volatile("" ::: "memory");  // keep the issue order
   // LDS part: wave instruction j moves vectors nreg + 64 j .. + 63 (lanes past
   // the row end read zeros and are never used).
   for (int j = wid; 64 * j < nlds; j += CP_NW)
     __builtin_amdgcn_raw_ptr_buffer_load_lds(rz, (__attribute__((address_space(3))) void*)&part[64 * j], 16,
                                              (uint32_t)(16 * (nreg + 64 * j + lane)), 0, 0, 2);
-  // Register part: slot s of thread tid holds vector s * CP_NT + tid.
-  // Lanes past the row end load zeros (out of range) and are skipped below.
-  u32x4 v[CP_RS];
+  asm volatile("" ::: "memory");
 #pragma unroll
-  for (int s = 0; s < CP_RS; ++s) {
+  for (int s = CP_RA; s < CP_RS; ++s) {
     const int i = s * CP_NT + tid;
     v[s] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
                                          rz, i < nreg ? (uint32_t)(16 * i) : CP_OOB, 0, 2));
   }
-  __builtin_amdgcn_s_waitcnt(0);  // this wave's DMA into LDS has landed
+  // Only part B's loads may still be outstanding: this wave's DMA into LDS
+  // and its part-A slots have landed.
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(CP_RS - CP_RA) : "memory");
   __syncthreads();
 
-  // Row maximum.
+  // ---- part A: maximum, then exp(z - m_A) once per logit (fp16, in place)
   float run = tail ? tail_sh[lane] : -INFINITY;
 #pragma unroll
-  for (int s = 0; s < CP_RS; ++s)
+  for (int s = 0; s < CP_RA; ++s)
     if (s * CP_NT + tid < nreg) run = fmaxf(run, vec_max(v[s]));
   for (int j = tid; j < nlds; j += CP_NT) run = fmaxf(run, vec_max(part[j]));
   {
     const float w = wave_max(run);
-    if (lane == 0) red[wid] = w;
+    if (lane == 0) red_a[wid] = w;
   }
   __syncthreads();
-  float m = red[0];
-  for (int w = 1; w < CP_NW; ++w) m = fmaxf(m, red[w]);
-  const float mL = m * LOG2E;
-  __syncthreads();  // red is reused for the sums
+  float mA = red_a[0];
+  for (int w = 1; w < CP_NW; ++w) mA = fmaxf(mA, red_a[w]);
   // Opaque to the compiler: otherwise it keeps the max pass's widened logits
   // alive for the exp pass, which needs far more registers than the row.
 #pragma unroll
-  for (int s = 0; s < CP_RS; ++s) asm volatile("" : "+v"(v[s]));
+  for (int s = 0; s < CP_RA; ++s) asm volatile("" : "+v"(v[s]));
   int t2 = tid;  // likewise for the per-slot offsets and masks derived from tid
   asm volatile("" : "+v"(t2));
 
-  // exp(z - m) once per logit, summed in fp32 and kept as fp16 in place.
-  const int vlim = OPT ? (int)o.vv : nvec * 8;
-  const bool y_ok = y >= 0 && y < vlim;
-  const float zy = y_ok ? __uint_as_float((uint32_t)logits[row * V + (y_ok ? y : 0)] << 16) : 0.f;
-  // (with smoothing, the same pass sums the vocabulary logits)
-  float sum = 0.f, zs = 0.f;
-  if (tail) {
-    const float zt = tail_sh[lane];
-    sum = __builtin_amdgcn_exp2f(zt * LOG2E - mL);
-    zs = zt;
-    tail_sh[lane] = sum;  // the same lane reads it back for the gradient
-  }
-  auto expv = [&](u32x4& x) {
+  // (with smoothing, the exp passes also sum the vocabulary logits)
+  float sumA = 0.f, sumB = 0.f, zs = 0.f;
+  auto expv = [&](u32x4& x, float mL, float& sum) {
     float ex[8];
 #pragma unroll
     for (int e = 0; e < 8; ++e) ex[e] = __builtin_amdgcn_exp2f(elem(x, e) * LOG2E - mL);
@@ -390,20 +396,56 @@ __global__ __launch_bounds__(CP_NT) __attribute__((amdgpu_waves_per_eu(4, 4))) v
 #pragma unroll
     for (int q = 0; q < 4; ++q) x[q] = pack_f16(ex[2 * q], ex[2 * q + 1]);
   };
-  // (the scheduling fences keep the compiler from overlapping slots, which
-  // would need registers the 88 data registers leave no room for)
+  {
+    const float mAL = mA * LOG2E;
+    if (tail) {
+      const float zt = tail_sh[lane];
+      sumA = __builtin_amdgcn_exp2f(zt * LOG2E - mAL);
+      zs = zt;
+      tail_sh[lane] = sumA;  // the same lane reads it back for the gradient
+    }
+    // (the scheduling fences keep the compiler from overlapping slots, which
+    // would need registers the 88 data registers leave no room for)
 #pragma unroll
-  for (int s = 0; s < CP_RS; ++s) {
-    if (s * CP_NT + t2 < nreg) expv(v[s]);
+    for (int s = 0; s < CP_RA; ++s) {
+      if (s * CP_NT + t2 < nreg) expv(v[s], mAL, sumA);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    for (int j = tid; j < nlds; j += CP_NT) {
+      u32x4 x = part[j];
+      expv(x, mAL, sumA);
+      part[j] = x;  // the same thread reads it back in the gradient pass
+    }
+  }
+
+  // ---- part B: the row maximum m, then exp(z - m)
+  run = -INFINITY;
+#pragma unroll
+  for (int s = CP_RA; s < CP_RS; ++s)
+    if (s * CP_NT + t2 < nreg) run = fmaxf(run, vec_max(v[s]));
+  {
+    const float w = wave_max(run);
+    if (lane == 0) red_b[wid] = w;
+  }
+  __syncthreads();
+  float m = mA;
+  for (int w = 0; w < CP_NW; ++w) m = fmaxf(m, red_b[w]);
+  const float mL = m * LOG2E;
+  const float fA = __builtin_amdgcn_exp2f((mA - m) * LOG2E);  // part A's values times fA are exp(z - m)
+#pragma unroll
+  for (int s = CP_RA; s < CP_RS; ++s) asm volatile("" : "+v"(v[s]));
+#pragma unroll
+  for (int s = CP_RA; s < CP_RS; ++s) {
+    if (s * CP_NT + t2 < nreg) expv(v[s], mL, sumB);
     __builtin_amdgcn_sched_barrier(0);
   }
-  for (int j = tid; j < nlds; j += CP_NT) {
-    u32x4 x = part[j];
-    expv(x);
-    part[j] = x;  // the same thread reads it back in the gradient pass
-  }
+
+  // exp(z - m) is fp16 in place; the row's values sum to s.
+  const int vlim = OPT ? (int)o.vv : nvec * 8;
+  const bool y_ok = y >= 0 && y < vlim;
+  const float zy = y_ok ? __uint_as_float((uint32_t)logits[row * V + (y_ok ? y : 0)] << 16) : 0.f;
   {
-    const float w = wave_sum(sum);
+    const float w = wave_sum(sumA * fA + sumB);
     if (lane == 0) red[wid] = w;
     if constexpr (SMOOTH) {
       const float wz = wave_sum(zs);
@@ -424,13 +466,14 @@ __global__ __launch_bounds__(CP_NT) __attribute__((amdgpu_waves_per_eu(4, 4))) v
   // Gradient, written once; the lane that wrote the vector holding the
   // target rewrites that element afterwards (program order).
   const float scale = inv / ssum;
+  const float scaleA = scale * fA;
   const float c = SMOOTH ? eps * inv / (float)vlim : 0.f;  // smoothing share of each vocabulary column
   const float cy = (1.f - eps) * inv;                       // the target's share
   const int vy = y_ok ? (int)(y >> 3) : -1;
-  auto grad = [&](const u32x4& x, int i) {
+  auto grad = [&](const u32x4& x, int i, float sc) {
     float g[8];
 #pragma unroll
-    for (int e = 0; e < 8; ++e) g[e] = SMOOTH ? f16_elem(x, e) * scale - c : f16_elem(x, e) * scale;
+    for (int e = 0; e < 8; ++e) g[e] = SMOOTH ? f16_elem(x, e) * sc - c : f16_elem(x, e) * sc;
     const u32x4 w{pack_bf16(g[0], g[1]), pack_bf16(g[2], g[3]), pack_bf16(g[4], g[5]), pack_bf16(g[6], g[7])};
     __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(__attribute__((ext_vector_type(4))) int, w), rd,
                                            (uint32_t)(16 * i), 0, 2);
@@ -441,13 +484,13 @@ __global__ __launch_bounds__(CP_NT) __attribute__((amdgpu_waves_per_eu(4, 4))) v
     const int i = s * CP_NT + t2;
     if (i < nreg) {
       owner |= i == vy;
-      grad(v[s], i);
+      grad(v[s], i, s < CP_RA ? scaleA : scale);
     }
     __builtin_amdgcn_sched_barrier(0);
   }
   for (int j = tid; j < nlds; j += CP_NT) {
     owner |= nreg + j == vy;
-    grad(part[j], nreg + j);
+    grad(part[j], nreg + j, scaleA);
   }
   if (owner) {
     const float gy = __builtin_amdgcn_exp2f(zy * LOG2E - mL) * scale - c - cy;
@@ -458,7 +501,7 @@ __global__ __launch_bounds__(CP_NT) __attribute__((amdgpu_waves_per_eu(4, 4))) v
     // padding vectors after it.
     if (rem > 0 && wid == 0 && lane < 8) {
       const int col = 8 * nfull + lane;
-      const float g = lane < rem ? tail_sh[lane] * scale - c - (col == y ? cy : 0.f) : 0.f;
+      const float g = lane < rem ? tail_sh[lane] * scaleA - c - (col == y ? cy : 0.f) : 0.f;
       dlogits[row * V + col] = __builtin_bit_cast(uint16_t, (__bf16)g);
     }
     for (int i = nfull + (rem > 0 ? 1 : 0) + tid; i < nvec; i += CP_NT)
