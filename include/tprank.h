@@ -158,8 +158,10 @@ int tp_mlp_fwd_bwd(int tp, int dtype, int w_layout, int64_t T, int64_t d, int64_
 /*
  * Bytes of workspace tp_mlp_act_fwd_bwd() needs.  Plain (gated == 0): as
  * tp_mlp_workspace_bytes().  Gated: five T x f buffers in `dtype` (gate and
- * up pre-activations, H, and their gradients), tp fp32 T x d partials of y
- * when tp > 1, and 2 tp fp32 T x d partials of dx.  0 for invalid arguments.
+ * up pre-activations, H, and their gradients), a d x 2f copy of the gate and
+ * up weights in `dtype` (each rank's columns side by side, so that its dx is
+ * one product), and, when tp > 1, tp fp32 T x d partials of y and of dx.
+ * 0 for invalid arguments.
  */
 size_t tp_mlp_act_workspace_bytes(int tp, int dtype, int gated, int64_t T, int64_t d, int64_t f);
 

@@ -260,8 +260,8 @@ size_t mlp_workspace(int tp, int dtype, bool gated, int64_t T, int64_t d, int64_
   const size_t tf = align256((size_t)(T * f * esize(dtype))), td = align256((size_t)(T * d * 4));
   if (!gated)  // sigma'(P) / dZ, H, partials, fp32 dH of the co-scheduled rows
     return 2 * tf + (tp > 1 ? 2 * (size_t)tp * td : 0) + align256((size_t)(cosched_rows(dtype, TPR_ACT_GELU, tp, T, f) * f * 4));
-  // gate, up, H, dA (dH first), dU; y partials when tp > 1; two dx partials per rank
-  return 5 * tf + (tp > 1 ? (size_t)tp * td : 0) + 2 * (size_t)tp * td;
+  // gate, up, H; [dA | dU] per rank (dH first); [W1_r | W3_r] per rank; y and dx partials when tp > 1
+  return 5 * tf + align256((size_t)(d * 2 * f * esize(dtype))) + (tp > 1 ? 2 * (size_t)tp * td : 0);
 }
 
 int check_act(int act) {
@@ -357,71 +357,95 @@ int mlp_plain(int tp, int dtype, bool math, int act, int64_t T, int64_t d, int64
 
 // Gated MLP: {A_r = X W1_r, U_r = X W3_r} | H = sigma(A) U | {Z_r = H_r W2_r,
 // dW2_r = H_r^T gy, dH_r = gy W2_r^T} | dA = dH U sigma'(A), dU = dH sigma(A)
-// | {dW1_r = X^T dA_r, dW3_r = X^T dU_r, dx_r = dA_r W1_r^T + dU_r W3_r^T}.
-// The two products of dx_r land in two partial slots summed with the ranks'.
+// | {dW1_r = X^T dA_r, dW3_r = X^T dU_r, dx_r = [dA_r | dU_r] [W1_r | W3_r]^T}.
+// dA_r and dU_r sit side by side (T x 2 f_r, dH written into the dA half),
+// and a copy of the rank's weight columns [W1_r | W3_r] makes dx_r one
+// product of inner size 2 f_r, written straight to dx for tp == 1.
 int mlp_gated(int tp, int dtype, bool math, int act, int64_t T, int64_t d, int64_t f, const void* x, const void* w1,
               const void* w3, const void* w2, const void* gy, float* y, float* dx, float* dw1, float* dw3, float* dw2,
               void* ws, hipStream_t s) {
   const int64_t e = esize(dtype);
   const size_t tf = align256((size_t)(T * f * e));
   char* wsb = static_cast<char*>(ws);
-  char* Ab = wsb;            // gate pre-activation
-  char* Ub = wsb + tf;       // up projection
-  char* Hb = wsb + 2 * tf;   // sigma(A) U
-  char* dAb = wsb + 3 * tf;  // dH, then dA in place
-  char* dUb = wsb + 4 * tf;
+  char* Ab = wsb;             // gate pre-activation, rank blocks T x f_r
+  char* Ub = wsb + tf;        // up projection
+  char* Hb = wsb + 2 * tf;    // sigma(A) U
+  char* dAUb = wsb + 3 * tf;  // rank blocks T x 2 f_r: [dH, then dA | dU]
+  char* Wc = wsb + 5 * tf;    // rank blocks of [W1_r | W3_r]: d x 2 f_r (math) or 2 f_r x d (torch)
   const int64_t pstride = (int64_t)(align256((size_t)(T * d * 4)) / 4);
-  float* zpart = reinterpret_cast<float*>(wsb + 5 * tf);
-  float* xpart = zpart + (tp > 1 ? (int64_t)tp * pstride : 0);
-  const bool ydirect = tp == 1;
+  float* zpart = reinterpret_cast<float*>(wsb + 5 * tf + align256((size_t)(d * 2 * f * e)));
+  float* xpart = zpart + (int64_t)tp * pstride;
+  const bool direct = tp == 1;
   const int raw = dtype == TPR_BF16 ? tpr::EPI_BF16 : tpr::EPI_F32;  // output in the compute dtype
-  int nslots = 0, nx = 0;
+  int nslots = 0;
+  struct Rank {
+    int64_t lo, fr;
+  };
+  std::vector<Rank> ranks;
   std::vector<Job> fwd1, mid, last;
   for (int r = 0; r < tp; ++r) {
     int64_t lo, hi;
     shard_of(f, tp, r, &lo, &hi);
     const int64_t fr = hi - lo;
     if (fr == 0) continue;
+    ranks.push_back(Rank{lo, fr});
     char* Ar = Ab + T * lo * e;
     char* Ur = Ub + T * lo * e;
     char* Hr = Hb + T * lo * e;
-    char* dAr = dAb + T * lo * e;
-    char* dUr = dUb + T * lo * e;
-    float* ydst = ydirect ? y : zpart + nslots * pstride;
-    float* xg = xpart + (nx++) * pstride;
-    float* xu = xpart + (nx++) * pstride;
-    if (math) {  // w1, w3 d x f, w2 f x d
+    char* dAr = dAUb + 2 * T * lo * e;  // T x 2 fr, dA in columns [0, fr), dU in [fr, 2 fr)
+    char* dUr = dAr + fr * e;
+    char* Wr = Wc + 2 * d * lo * e;
+    float* ydst = direct ? y : zpart + nslots * pstride;
+    float* xdst = direct ? dx : xpart + nslots * pstride;
+    if (math) {  // w1, w3 d x f, w2 f x d; Wr is d x 2 fr
       fwd1.push_back(job(prob(x, d, 1, cb(w1) + lo * e, f, 1, Ar, fr, T, fr, d), true, false, raw));
       fwd1.push_back(job(prob(x, d, 1, cb(w3) + lo * e, f, 1, Ur, fr, T, fr, d), true, false, raw));
       mid.push_back(job(prob(Hr, fr, 1, cb(w2) + lo * d * e, d, 1, ydst, d, T, d, fr), true, false, tpr::EPI_F32));
       mid.push_back(job(prob(Hr, 1, fr, gy, d, 1, dw2 + lo * d, d, fr, d, T), false, false, tpr::EPI_F32));
-      mid.push_back(job(prob(gy, d, 1, cb(w2) + lo * d * e, 1, d, dAr, fr, T, fr, d), true, true, raw));
-      last.push_back(job(prob(x, 1, d, dAr, fr, 1, dw1 + lo, f, d, fr, T), false, false, tpr::EPI_F32));
-      last.push_back(job(prob(x, 1, d, dUr, fr, 1, dw3 + lo, f, d, fr, T), false, false, tpr::EPI_F32));
-      last.push_back(job(prob(dAr, fr, 1, cb(w1) + lo * e, 1, f, xg, d, T, d, fr), true, true, tpr::EPI_F32));
-      last.push_back(job(prob(dUr, fr, 1, cb(w3) + lo * e, 1, f, xu, d, T, d, fr), true, true, tpr::EPI_F32));
-    } else {  // w1, w3 (f, d), w2 (d, f)
+      mid.push_back(job(prob(gy, d, 1, cb(w2) + lo * d * e, 1, d, dAr, 2 * fr, T, fr, d), true, true, raw));
+      last.push_back(job(prob(x, 1, d, dAr, 2 * fr, 1, dw1 + lo, f, d, fr, T), false, false, tpr::EPI_F32));
+      last.push_back(job(prob(x, 1, d, dUr, 2 * fr, 1, dw3 + lo, f, d, fr, T), false, false, tpr::EPI_F32));
+      last.push_back(job(prob(dAr, 2 * fr, 1, Wr, 1, 2 * fr, xdst, d, T, d, 2 * fr), true, true, tpr::EPI_F32));
+    } else {  // w1, w3 (f, d), w2 (d, f); Wr is 2 fr x d
       fwd1.push_back(job(prob(x, d, 1, cb(w1) + lo * d * e, 1, d, Ar, fr, T, fr, d), true, true, raw));
       fwd1.push_back(job(prob(x, d, 1, cb(w3) + lo * d * e, 1, d, Ur, fr, T, fr, d), true, true, raw));
       mid.push_back(job(prob(Hr, fr, 1, cb(w2) + lo * e, 1, f, ydst, d, T, d, fr), true, true, tpr::EPI_F32));
       mid.push_back(job(prob(gy, 1, d, Hr, fr, 1, dw2 + lo, f, d, fr, T), false, false, tpr::EPI_F32));
-      mid.push_back(job(prob(gy, d, 1, cb(w2) + lo * e, f, 1, dAr, fr, T, fr, d), true, false, raw));
-      last.push_back(job(prob(dAr, 1, fr, x, d, 1, dw1 + lo * d, d, fr, d, T), false, false, tpr::EPI_F32));
-      last.push_back(job(prob(dUr, 1, fr, x, d, 1, dw3 + lo * d, d, fr, d, T), false, false, tpr::EPI_F32));
-      last.push_back(job(prob(dAr, fr, 1, cb(w1) + lo * d * e, d, 1, xg, d, T, d, fr), true, false, tpr::EPI_F32));
-      last.push_back(job(prob(dUr, fr, 1, cb(w3) + lo * d * e, d, 1, xu, d, T, d, fr), true, false, tpr::EPI_F32));
+      mid.push_back(job(prob(gy, d, 1, cb(w2) + lo * e, f, 1, dAr, 2 * fr, T, fr, d), true, false, raw));
+      last.push_back(job(prob(dAr, 1, 2 * fr, x, d, 1, dw1 + lo * d, d, fr, d, T), false, false, tpr::EPI_F32));
+      last.push_back(job(prob(dUr, 1, 2 * fr, x, d, 1, dw3 + lo * d, d, fr, d, T), false, false, tpr::EPI_F32));
+      last.push_back(job(prob(dAr, 2 * fr, 1, Wr, d, 1, xdst, d, T, d, 2 * fr), true, false, tpr::EPI_F32));
     }
     ++nslots;
   }
   hipError_t he;
+  // The rank's weight columns side by side (independent of everything else).
+  for (const Rank& rk : ranks) {
+    char* Wr = Wc + 2 * d * rk.lo * e;
+    if (math) {  // rows of W1[:, lo:hi] then W3[:, lo:hi]
+      if ((he = tpr::launch_copy_2d(Wr, 2 * rk.fr * e, cb(w1) + rk.lo * e, f * e, d, rk.fr * e, s)) != hipSuccess ||
+          (he = tpr::launch_copy_2d(Wr + rk.fr * e, 2 * rk.fr * e, cb(w3) + rk.lo * e, f * e, d, rk.fr * e, s)) !=
+              hipSuccess)
+        return hip_fail(he, "gate / up weight copy");
+    } else {  // rows lo..hi of w1, then of w3
+      if ((he = tpr::launch_copy_2d(Wr, d * e, cb(w1) + rk.lo * d * e, d * e, rk.fr, d * e, s)) != hipSuccess ||
+          (he = tpr::launch_copy_2d(Wr + rk.fr * d * e, d * e, cb(w3) + rk.lo * d * e, d * e, rk.fr, d * e, s)) !=
+              hipSuccess)
+        return hip_fail(he, "gate / up weight copy");
+    }
+  }
   if ((he = run_jobs(fwd1, dtype, s)) != hipSuccess) return hip_fail(he, "gate / up GEMMs");
   if ((he = tpr::launch_glu_fwd(dtype, Ab, Ub, Hb, T * f, act, s)) != hipSuccess) return hip_fail(he, "gate * up");
   if ((he = run_jobs(mid, dtype, s)) != hipSuccess) return hip_fail(he, "down / dW2 / dH GEMMs");
-  if ((he = tpr::launch_glu_bwd(dtype, dAb, Ab, Ub, dUb, T * f, act, s)) != hipSuccess)
-    return hip_fail(he, "gate / up gradients");
+  for (const Rank& rk : ranks) {
+    char* dAr = dAUb + 2 * T * rk.lo * e;
+    if ((he = tpr::launch_glu_bwd_2d(dtype, dAr, Ab + T * rk.lo * e, Ub + T * rk.lo * e, dAr + rk.fr * e, T, rk.fr,
+                                     2 * rk.fr, act, s)) != hipSuccess)
+      return hip_fail(he, "gate / up gradients");
+  }
   if ((he = run_jobs(last, dtype, s)) != hipSuccess) return hip_fail(he, "dW1 / dW3 / dx GEMMs");
-  if ((he = finish_sum(y, T, d, zpart, nslots, pstride, ydirect, s)) != hipSuccess) return hip_fail(he, "y reduction");
-  if ((he = finish_sum(dx, T, d, xpart, nx, pstride, false, s)) != hipSuccess) return hip_fail(he, "dx reduction");
+  if ((he = finish_sum(y, T, d, zpart, nslots, pstride, direct, s)) != hipSuccess) return hip_fail(he, "y reduction");
+  if ((he = finish_sum(dx, T, d, xpart, nslots, pstride, direct, s)) != hipSuccess) return hip_fail(he, "dx reduction");
   return TPR_OK;
 }
 

@@ -74,6 +74,13 @@ hipError_t launch_fill_zero(float* out, int64_t rows, int64_t cols, int64_t ld, 
 hipError_t launch_glu_fwd(int dtype, const void* A, const void* U, void* H, int64_t n, int act, hipStream_t s);
 hipError_t launch_glu_bwd(int dtype, void* dA, const void* A, const void* U, void* dU, int64_t n, int act,
                           hipStream_t s);
+// The same backward over a rows x cols block whose dH / dA and dU rows are
+// `ld` elements apart (A and U are contiguous rows of cols).
+hipError_t launch_glu_bwd_2d(int dtype, void* dA, const void* A, const void* U, void* dU, int64_t rows, int64_t cols,
+                             int64_t ld, int act, hipStream_t s);
+// Copy rows x row_bytes from src (rows ld_src bytes apart) to dst (ld_dst).
+hipError_t launch_copy_2d(void* dst, int64_t ld_dst, const void* src, int64_t ld_src, int64_t rows, int64_t row_bytes,
+                          hipStream_t s);
 // dst = dst * src over n contiguous elements: dst in `dtype` (16-byte
 // aligned), src fp32; the product is rounded once to `dtype`.
 hipError_t launch_mul_f32_into(int dtype, void* dst, const float* src, int64_t n, hipStream_t s);

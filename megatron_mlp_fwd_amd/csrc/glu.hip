@@ -172,6 +172,71 @@ __global__ __launch_bounds__(256) void mul_f32_into_f32(float* __restrict__ dst,
   for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < n; i += stride) dst[i] *= src[i];
 }
 
+// dA / dU of a rows x cols block: dH and the outputs rows `ld` apart, A and
+// U contiguous.  VEC: 8 bf16 per thread (cols % 8 == 0, 16-byte aligned).
+template <typename T, bool VEC>
+__global__ __launch_bounds__(256) void glu_bwd_2d_kernel(T* __restrict__ dA, const T* __restrict__ A,
+                                                         const T* __restrict__ U, T* __restrict__ dU, int64_t rows,
+                                                         int64_t cols, int64_t ld, int act) {
+  const int64_t per_row = VEC ? cols / 8 : cols;
+  const int64_t n = rows * per_row;
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < n; i += stride) {
+    const int64_t r = i / per_row, c = (i - r * per_row) * (VEC ? 8 : 1);
+    T* ga = dA + r * ld + c;
+    T* gu = dU + r * ld + c;
+    const T* a = A + r * cols + c;
+    const T* u = U + r * cols + c;
+    if constexpr (VEC) {
+      const u32x4 g = *reinterpret_cast<const u32x4*>(ga);
+      const u32x4 av = *reinterpret_cast<const u32x4*>(a);
+      const u32x4 uv = *reinterpret_cast<const u32x4*>(u);
+      u32x4 oa, ou;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        float s0, d0, s1, d1;
+        act_eval(act, bf_lo(av[q]), s0, d0);
+        act_eval(act, bf_hi(av[q]), s1, d1);
+        const float g0 = bf_lo(g[q]), g1 = bf_hi(g[q]);
+        oa[q] = pack2(g0 * bf_lo(uv[q]) * d0, g1 * bf_hi(uv[q]) * d1);
+        ou[q] = pack2(g0 * s0, g1 * s1);
+      }
+      *reinterpret_cast<u32x4*>(ga) = oa;
+      *reinterpret_cast<u32x4*>(gu) = ou;
+    } else if constexpr (sizeof(T) == 2) {
+      float sv, dv;
+      act_eval(act, bf(*a), sv, dv);
+      const float g = bf(*ga);
+      *ga = to_bf(g * bf(*u) * dv);
+      *gu = to_bf(g * sv);
+    } else {
+      float sv, dv;
+      act_eval_f32(act, *a, sv, dv);
+      const float g = *ga;
+      *ga = g * *u * dv;
+      *gu = g * sv;
+    }
+  }
+}
+
+// rows x row_bytes, 16 bytes (VEC) or 2 bytes per thread and iteration.
+template <bool VEC>
+__global__ __launch_bounds__(256) void copy_2d_kernel(char* __restrict__ dst, int64_t ld_dst,
+                                                      const char* __restrict__ src, int64_t ld_src, int64_t rows,
+                                                      int64_t row_bytes) {
+  constexpr int W = VEC ? 16 : 2;
+  const int64_t per_row = row_bytes / W;
+  const int64_t n = rows * per_row;
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < n; i += stride) {
+    const int64_t r = i / per_row, c = (i - r * per_row) * W;
+    if constexpr (VEC)
+      *reinterpret_cast<u32x4*>(dst + r * ld_dst + c) = *reinterpret_cast<const u32x4*>(src + r * ld_src + c);
+    else
+      *reinterpret_cast<uint16_t*>(dst + r * ld_dst + c) = *reinterpret_cast<const uint16_t*>(src + r * ld_src + c);
+  }
+}
+
 unsigned grid_for(int64_t nvec) {
   const int64_t b = (nvec + 255) / 256;
   return (unsigned)(b < 1 ? 1 : (b > 4096 ? 4096 : b));
@@ -201,6 +266,43 @@ hipError_t launch_glu_bwd(int dtype, void* dA, const void* A, const void* U, voi
   else
     hipLaunchKernelGGL(glu_bwd_f32, dim3(grid_for(n / 4)), dim3(256), 0, s, static_cast<float*>(dA),
                        static_cast<const float*>(A), static_cast<const float*>(U), static_cast<float*>(dU), n, act);
+  return hipGetLastError();
+}
+
+hipError_t launch_glu_bwd_2d(int dtype, void* dA, const void* A, const void* U, void* dU, int64_t rows, int64_t cols,
+                             int64_t ld, int act, hipStream_t s) {
+  if (rows <= 0 || cols <= 0) return hipSuccess;
+  if (dtype == 1) {
+    const bool vec = cols % 8 == 0 && ld % 8 == 0 && reinterpret_cast<uintptr_t>(dA) % 16 == 0 &&
+                     reinterpret_cast<uintptr_t>(A) % 16 == 0 && reinterpret_cast<uintptr_t>(U) % 16 == 0 &&
+                     reinterpret_cast<uintptr_t>(dU) % 16 == 0;
+    uint16_t *ga = static_cast<uint16_t*>(dA), *gu = static_cast<uint16_t*>(dU);
+    const uint16_t *a = static_cast<const uint16_t*>(A), *u = static_cast<const uint16_t*>(U);
+    if (vec)
+      hipLaunchKernelGGL((glu_bwd_2d_kernel<uint16_t, true>), dim3(grid_for(rows * cols / 8)), dim3(256), 0, s, ga, a,
+                         u, gu, rows, cols, ld, act);
+    else
+      hipLaunchKernelGGL((glu_bwd_2d_kernel<uint16_t, false>), dim3(grid_for(rows * cols)), dim3(256), 0, s, ga, a, u,
+                         gu, rows, cols, ld, act);
+  } else {
+    hipLaunchKernelGGL((glu_bwd_2d_kernel<float, false>), dim3(grid_for(rows * cols)), dim3(256), 0, s,
+                       static_cast<float*>(dA), static_cast<const float*>(A), static_cast<const float*>(U),
+                       static_cast<float*>(dU), rows, cols, ld, act);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_copy_2d(void* dst, int64_t ld_dst, const void* src, int64_t ld_src, int64_t rows, int64_t row_bytes,
+                          hipStream_t s) {
+  if (rows <= 0 || row_bytes <= 0) return hipSuccess;
+  const bool vec = row_bytes % 16 == 0 && ld_dst % 16 == 0 && ld_src % 16 == 0 &&
+                   reinterpret_cast<uintptr_t>(dst) % 16 == 0 && reinterpret_cast<uintptr_t>(src) % 16 == 0;
+  if (vec)
+    hipLaunchKernelGGL(copy_2d_kernel<true>, dim3(grid_for(rows * row_bytes / 16)), dim3(256), 0, s,
+                       static_cast<char*>(dst), ld_dst, static_cast<const char*>(src), ld_src, rows, row_bytes);
+  else
+    hipLaunchKernelGGL(copy_2d_kernel<false>, dim3(grid_for(rows * row_bytes / 2)), dim3(256), 0, s,
+                       static_cast<char*>(dst), ld_dst, static_cast<const char*>(src), ld_src, rows, row_bytes);
   return hipGetLastError();
 }
 

@@ -151,8 +151,9 @@ def test_mlp_act_workspace_and_bad_arguments(lib):
     ws = lib.tp_mlp_act_workspace_bytes
     T, d, f = 8192, 8192, 3584
     assert ws(1, 1, 0, T, d, f) == lib.tp_mlp_workspace_bytes(1, 1, T, d, f)
-    assert ws(1, 1, 1, T, d, f) == 5 * T * f * 2 + 2 * T * d * 4            # gated, one rank
-    assert ws(4, 1, 1, T, d, f) == 5 * T * f * 2 + (4 + 8) * T * d * 4      # y and 2 x dx partials per rank
+    # gated: gate, up, H, [dA | dU] (T x f each, bf16), [W1_r | W3_r] (d x 2f), y / dx partials when tp > 1
+    assert ws(1, 1, 1, T, d, f) == 5 * T * f * 2 + d * 2 * f * 2
+    assert ws(4, 1, 1, T, d, f) == 5 * T * f * 2 + d * 2 * f * 2 + 2 * 4 * T * d * 4
     assert ws(0, 1, 1, T, d, f) == 0
     fn = lib.tp_mlp_act_fwd_bwd
     p = ctypes.c_void_p(16)  # never dereferenced: validation stops first
