@@ -33,10 +33,11 @@ __device__ __forceinline__ void static_for(F&& f) {
   }
 }
 
+// One v_cvt_pk_bf16_f32 (round to nearest even) per pair.
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ uint32_t pack_bf16(float a, float b) {
-  const uint32_t x = __builtin_bit_cast(uint16_t, (__bf16)a);
-  const uint32_t y = __builtin_bit_cast(uint16_t, (__bf16)b);
-  return x | (y << 16);
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2_t{a, b}, bf16x2_t));
 }
 __device__ __forceinline__ float bf_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }

@@ -22,7 +22,12 @@ __device__ __forceinline__ float bf(uint16_t h) { return __uint_as_float((uint32
 __device__ __forceinline__ uint16_t to_bf(float x) { return __builtin_bit_cast(uint16_t, (__bf16)x); }
 __device__ __forceinline__ float bf_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
-__device__ __forceinline__ uint32_t pack2(float a, float b) { return (uint32_t)to_bf(a) | ((uint32_t)to_bf(b) << 16); }
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+// One v_cvt_pk_bf16_f32 (round to nearest even) per pair.
+__device__ __forceinline__ uint32_t pack2(float a, float b) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2_t{a, b}, bf16x2_t));
+}
 
 // bf16: fast fp32 activations (results rounded to bf16 anyway).
 __global__ __launch_bounds__(256) void glu_fwd_bf16(const uint16_t* __restrict__ A, const uint16_t* __restrict__ U,

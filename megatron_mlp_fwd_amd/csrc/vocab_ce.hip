@@ -84,15 +84,17 @@ __device__ __forceinline__ float wave_sum(float v) {
 
 __device__ __forceinline__ float lo16(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float hi16(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+// Pairs are converted as two-element vectors: one v_cvt_pk_bf16_f32 /
+// v_cvt_pk_f16_f32 (round to nearest even) instead of two single conversions,
+// a shift and an or.
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ uint32_t pack_bf16(float a, float b) {
-  const uint32_t x = __builtin_bit_cast(uint16_t, (__bf16)a);
-  const uint32_t y = __builtin_bit_cast(uint16_t, (__bf16)b);
-  return x | (y << 16);
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2_t{a, b}, bf16x2_t));
 }
 __device__ __forceinline__ uint32_t pack_f16(float a, float b) {
-  const uint32_t x = __builtin_bit_cast(uint16_t, (_Float16)a);
-  const uint32_t y = __builtin_bit_cast(uint16_t, (_Float16)b);
-  return x | (y << 16);
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2_t{a, b}, f16x2_t));
 }
 __device__ __forceinline__ float f16_elem(const u32x4& v, int e) {
   const uint32_t w = v[e >> 1];
