@@ -12,9 +12,11 @@ Inputs are resident in HBM before timing starts.  ``value`` is the MLP's
 fwd+bwd TFLOP/s (12*T*d*f algorithmic FLOP per call); the CE's algorithmic
 GB/s (2 bytes read + 2 bytes written per logit) and the inner GEMM's TFLOP/s
 are reported beside it.  Each call is timed with HIP events on the stream the
-library launches on.
+library launches on.  After the timed steps, torch's copy_ of the logits (the
+CE's bytes, read once and written once) is timed as the copy-rate context of
+the CE figure (``roofline_ce.copy_same_bytes_gbs``).
 
-Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline] [--copy-bytes N]
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline] [--copy-runs N] [--copy-bytes N]
        python bench.py --traffic-from FETCH_CSV WRITE_CSV COPY_BYTES
 The second form turns two rocprofv3 counter runs of the first form (one with
 --pmc FETCH_SIZE, one with --pmc WRITE_SIZE, both with --copy-bytes) into
@@ -360,6 +362,9 @@ def main():
     ap.add_argument("--small-runs", type=int, default=100,
                     help="timed calls per small (latency-bound) configuration and of the CE (0 = skip)")
     ap.add_argument("--traffic-from", nargs=3, metavar=("FETCH_CSV", "WRITE_CSV", "COPY_BYTES"))
+    ap.add_argument("--copy-runs", type=int, default=20,
+                    help="time this many torch copy_ calls of the CE's logits (median) as the copy-rate context "
+                         "of the CE figure; 0 skips")
     ap.add_argument("--copy-bytes", type=int, default=0,
                     help="also run one plain copy kernel (torch.neg on fp32) of this many bytes before timing, "
                          "so that profiler byte counters can be calibrated against a known size")
@@ -446,6 +451,25 @@ def main():
     gemm_traffic = stored_traffic(GEMM_KERNEL + "_bytes_per_launch")
     ce_traffic = stored_traffic(CE_KERNEL + "_bytes_per_launch")
 
+    # Context for the CE's HBM figure: a plain copy of the same bytes (torch's
+    # copy_ of the logits into the dlogits buffer), timed after the step loop
+    # on the same device.  The CE cannot beat what the HBM gives a copy.
+    copy_gbs = None
+    if args.copy_runs > 0:
+        src, dst = logits, ce_out[1]
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        cms = []
+        for _ in range(args.copy_runs):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            dst.copy_(src)
+            e1.record()
+            e1.synchronize()
+            cms.append(e0.elapsed_time(e1))
+        copy_gbs = ce_bytes / (sorted(cms)[len(cms) // 2] * 1e-3) / 1e9
+
     head = None
     if args.head_steps > 0:
         head = bench_head(tpr, workloads, dev, args.head_steps)
@@ -520,6 +544,8 @@ def main():
             "unit": "GB/s",
             "frac": round(ce_gbs / PEAK_HBM_GBS, 4),
             "traffic": ce_traffic,
+            "copy_same_bytes_gbs": None if copy_gbs is None else round(copy_gbs, 1),
+            "frac_of_copy": None if copy_gbs is None else round(ce_gbs / copy_gbs, 4),
         },
         "kernel_source_digest": kernel_source_digest(),
     }
