@@ -14,9 +14,12 @@ GB/s (2 bytes read + 2 bytes written per logit) and the inner GEMM's TFLOP/s
 are reported beside it.  Each call is timed with HIP events on the stream the
 library launches on.  After the timed steps, torch's copy_ of the logits (the
 CE's bytes, read once and written once) is timed as the copy-rate context of
-the CE figure (``roofline_ce.copy_same_bytes_gbs``).
+the CE figure (``roofline_ce.copy_same_bytes_gbs``), and the MLP's six
+products through torch.mm (hipBLASLt) as library context
+(``mlp_gemms_via_torch_mm``).
 
-Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline] [--copy-runs N] [--copy-bytes N]
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline] [--copy-runs N] [--blas-runs N]
+                       [--copy-bytes N]
        python bench.py --traffic-from FETCH_CSV WRITE_CSV COPY_BYTES
 The second form turns two rocprofv3 counter runs of the first form (one with
 --pmc FETCH_SIZE, one with --pmc WRITE_SIZE, both with --copy-bytes) into
@@ -362,6 +365,9 @@ def main():
     ap.add_argument("--small-runs", type=int, default=100,
                     help="timed calls per small (latency-bound) configuration and of the CE (0 = skip)")
     ap.add_argument("--traffic-from", nargs=3, metavar=("FETCH_CSV", "WRITE_CSV", "COPY_BYTES"))
+    ap.add_argument("--blas-runs", type=int, default=5,
+                    help="time the MLP's six products through torch.mm this many times (median) as library "
+                         "context; 0 skips")
     ap.add_argument("--copy-runs", type=int, default=20,
                     help="time this many torch copy_ calls of the CE's logits (median) as the copy-rate context "
                          "of the CE figure; 0 skips")
@@ -470,6 +476,36 @@ def main():
             cms.append(e0.elapsed_time(e1))
         copy_gbs = ce_bytes / (sorted(cms)[len(cms) // 2] * 1e-3) / 1e9
 
+    # Context for the GEMM figure: the MLP's six products through torch.mm
+    # (hipBLASLt, bf16 results, so less output traffic than the fp32 results
+    # of the library's call) at the same shapes and layouts, on the same
+    # device after the timed steps.  A library measurement, not the product.
+    blas = None
+    if args.blas_runs > 0:
+        Hb = torch.randn(T, f, device=dev).bfloat16()
+        def blas_call():
+            torch.mm(x, w1)                # P = x W1
+            torch.mm(Hb, w2)               # y = H W2
+            torch.mm(Hb.t(), gy)           # dW2 = H^T G
+            torch.mm(gy, w2.t())           # dH = G W2^T
+            torch.mm(x.t(), Hb)            # dW1 = x^T dZ
+            torch.mm(Hb, w1.t())           # dx = dZ W1^T
+        for _ in range(2):
+            blas_call()
+        torch.cuda.synchronize()
+        bms = []
+        for _ in range(args.blas_runs):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            blas_call()
+            e1.record()
+            e1.synchronize()
+            bms.append(e0.elapsed_time(e1))
+        bmed = sorted(bms)[len(bms) // 2]
+        blas = {"op": "torch.mm x 6 (hipBLASLt), bf16 results, the MLP's shapes and layouts",
+                "ms_median": round(bmed, 4), "tflops": round(mlp_flop / (bmed * 1e-3) / 1e12, 2)}
+        del Hb
+
     head = None
     if args.head_steps > 0:
         head = bench_head(tpr, workloads, dev, args.head_steps)
@@ -518,6 +554,7 @@ def main():
         "inner_gemm_tflops": round(inner_tflops, 2),
         "inner_gemm_ms": round(avg(inner_ms), 4),
         "inner_gemm_ms_min": round(min(inner_ms), 4),
+        "mlp_gemms_via_torch_mm": blas,
         "vocab_ce_gbs": round(ce_gbs, 1),
         "vocab_ce_pct_of_hbm_peak": round(100.0 * ce_gbs / PEAK_HBM_GBS, 2),
         "vocab_ce_ms": round(avg(ce_ms), 4),
