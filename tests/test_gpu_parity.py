@@ -209,7 +209,8 @@ def test_mlp_fp32_uneven_and_empty_ranks(tpr, tp, layout):
 
 @pytest.mark.parametrize("layout", ["math", "torch"])
 @pytest.mark.parametrize("tp", [1, 2, 3])
-@pytest.mark.parametrize("shape", [(512, 256, 256), (300, 264, 200), (64, 40, 24), (96, 512, 768)])
+@pytest.mark.parametrize("shape", [(512, 256, 256), (300, 264, 200), (64, 40, 24), (96, 512, 768), (272, 320, 448),
+                                   (256, 256, 232)])
 def test_mlp_bf16_tiles_and_tails(tpr, shape, tp, layout, gemm_path):
     say("TP MLP bf16", shape, tp, layout, gemm_path)
     T, d, f = shape
