@@ -58,10 +58,12 @@ def kernel_source_digest():
     return h.hexdigest()[:16]
 
 
-def stored_traffic(kernel):
+TRAFFIC_JSON = os.path.join(ROOT, "profiles", "traffic.json")
+
+
+def stored_traffic(kernel, path=TRAFFIC_JSON):
     """HBM bytes per launch measured with rocprofv3 counters for the current
     kernel sources, or None when the sources changed since."""
-    path = os.path.join(ROOT, "profiles", "traffic.json")
     try:
         with open(path) as f:
             t = json.load(f)
@@ -78,7 +80,7 @@ CE_KERNEL = "ce_pair_kernel"
 COPY_KERNEL = "neg_kernel"
 
 
-def traffic_from(fetch_csv, write_csv, copy_bytes):
+def traffic_from(fetch_csv, write_csv, copy_bytes, out_path=TRAFFIC_JSON):
     """HBM bytes per launch from rocprofv3 counter_collection CSVs.
 
     FETCH_SIZE / WRITE_SIZE are reported in KiB per dispatch; each is scaled
@@ -110,11 +112,11 @@ def traffic_from(fetch_csv, write_csv, copy_bytes):
     for kernel in (GEMM_KERNEL, CE_KERNEL):
         out[kernel + "_bytes_per_launch"] = (out["FETCH_SIZE"][kernel]["avg_bytes"] +
                                              out["WRITE_SIZE"][kernel]["avg_bytes"])
-    path = os.path.join(ROOT, "profiles", "traffic.json")
-    with open(path, "w") as f:
+    with open(out_path, "w") as f:
         json.dump(out, f, indent=1)
         f.write("\n")
     print(json.dumps(out, indent=1))
+    return out
 
 
 def cpu_baseline(budget_s=10.0, max_reps=4):
