@@ -313,6 +313,38 @@ def bench_attn_proj(tpr, dev, steps):
             "pct_of_bf16_peak": round(100.0 * tflops / PEAK_BF16_TFLOPS, 2), "flop_per_call": flop}
 
 
+def bench_ce_stats(tpr, workloads, dev, steps):
+    """The vocabulary-parallel CE of the main step with the per-shard
+    statistics (m_r, s_r, t_r for every row and shard, the simulated ranks'
+    partial results) also written out.  Algorithmic bytes: the CE's 2 read +
+    2 written per logit, plus 12 per row and shard."""
+    import torch
+
+    logits, labels = workloads.vocab_ce(T=CE["T"], V=CE["V"], seed=2, device=dev)
+    out = (torch.empty((), device=dev), torch.empty_like(logits),
+           torch.empty(CE["T"], CE["parts"], 3, device=dev))
+    ws = torch.empty(tpr.vocab_parallel_ce_workspace_bytes(CE["parts"], CE["T"], CE["V"]), dtype=torch.uint8,
+                     device=dev)
+    call = lambda: tpr.vocab_parallel_ce_fwd_bwd(CE["parts"], logits, labels, shard_stats=True, out=out,
+                                                 workspace=ws)
+    for _ in range(2):
+        call()
+    torch.cuda.synchronize()
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(steps)]
+    for e in ev:
+        e[0].record()
+        call()
+        e[1].record()
+    torch.cuda.synchronize()
+    ms = sorted(e[0].elapsed_time(e[1]) for e in ev)
+    nbytes = 4.0 * CE["T"] * CE["V"] + 12.0 * CE["T"] * CE["parts"]
+    mean = sum(ms) / len(ms)
+    gbs = nbytes / (mean * 1e-3) / 1e9
+    return {"config": dict(CE, dtype="bf16", shard_stats=True), "steps": steps, "ms": round(mean, 4),
+            "ms_min": round(ms[0], 4), "gbs": round(gbs, 1), "pct_of_hbm_peak": round(100.0 * gbs / PEAK_HBM_GBS, 2),
+            "bytes_per_call": nbytes}
+
+
 def bench_ce_opts(tpr, workloads, dev, steps):
     """The cross-entropy with options: a 128000-entry vocabulary padded to
     128256 columns, 8 shards, label smoothing 0.1, about one position in
@@ -358,6 +390,8 @@ def main():
                     help="timed calls of the vocabulary-parallel output head + CE (reported beside the step; 0 = skip)")
     ap.add_argument("--mlp-8b-steps", type=int, default=10,
                     help="timed calls of the 8B-rank MLP fwd+bwd (reported beside the step; 0 = skip)")
+    ap.add_argument("--ce-stats-steps", type=int, default=10,
+                    help="timed calls of the CE with per-shard statistics written out (0 skips)")
     ap.add_argument("--ce-opts-steps", type=int, default=10,
                     help="timed calls of the cross-entropy with options (reported beside the step; 0 = skip)")
     ap.add_argument("--gated-steps", type=int, default=5,
@@ -523,6 +557,9 @@ def main():
     gated = None
     if args.gated_steps > 0:
         gated = bench_gated_mlp(tpr, dev, args.gated_steps)
+    ce_stats = None
+    if args.ce_stats_steps > 0:
+        ce_stats = bench_ce_stats(tpr, workloads, dev, args.ce_stats_steps)
     ce_opts = None
     if args.ce_opts_steps > 0:
         ce_opts = bench_ce_opts(tpr, workloads, dev, args.ce_opts_steps)
@@ -592,6 +629,8 @@ def main():
         line["vocab_head_ce"] = head
     if mlp_8b is not None:
         line["mlp_8b_rank"] = mlp_8b
+    if ce_stats is not None:
+        line["vocab_ce_shard_stats"] = ce_stats
     if ce_opts is not None:
         line["vocab_ce_opts"] = ce_opts
     if gated is not None:
