@@ -32,6 +32,10 @@
 //
 // A final single-workgroup kernel averages the per-row losses in a fixed
 // order (fp64 accumulation).
+#include <cstdlib>
+#include <cstring>
+#include <type_traits>
+
 #include "common.h"
 
 namespace tpr {
@@ -277,8 +281,12 @@ struct CeOpt {
   int64_t ignore;        // label of ignored rows
   float eps;             // label smoothing
   const float* inv_cnt;  // 1 / counted rows, written by ce_count_kernel
+  float* stats;          // CE_STATS: T x P x {m_r, s_r, t_r}
+  int P;                 // CE_STATS: shards, each vps 8-logit vectors
+  int vps;
+  uint32_t vps_magic;    // floor((2^32 - 1) / vps) + 1: i / vps = umulhi(i, magic) for i, vps < 2^16
 };
-enum { CE_PLAIN = 0, CE_OPT = 1, CE_OPT_SMOOTH = 2 };
+enum { CE_PLAIN = 0, CE_OPT = 1, CE_OPT_SMOOTH = 2, CE_STATS = 3 };
 
 // ---------------------------------------------------------------- paired path
 // Rows without per-shard statistics, bf16: two 512-thread workgroups per CU,
@@ -298,8 +306,13 @@ template <int MODE>
 __global__ __launch_bounds__(CP_NT) __attribute__((amdgpu_waves_per_eu(4, 4))) void ce_pair_kernel(
     const uint16_t* __restrict__ logits, const int64_t* __restrict__ labels, uint16_t* __restrict__ dlogits,
     float* __restrict__ row_loss, int64_t V, float invT, CeOpt o) {
-  constexpr bool OPT = MODE != CE_PLAIN, SMOOTH = MODE == CE_OPT_SMOOTH;
+  constexpr bool OPT = MODE == CE_OPT || MODE == CE_OPT_SMOOTH, SMOOTH = MODE == CE_OPT_SMOOTH;
+  constexpr bool STATS = MODE == CE_STATS;
   __shared__ __attribute__((aligned(1024))) u32x4 part[CP_LDS_VEC];
+  // CE_STATS: per wave and shard, the maximum and the part A / part B sums
+  // (each wave writes only its own row; the rows are combined in order).
+  constexpr int TABW = CP_NW * CE_PMAX;
+  __shared__ float tab[STATS ? 3 * TABW : 1];
   __shared__ float red[CP_NW];
   __shared__ float red_a[CP_NW];
   __shared__ float red_b[CP_NW];
@@ -333,6 +346,50 @@ __global__ __launch_bounds__(CP_NT) __attribute__((amdgpu_waves_per_eu(4, 4))) v
   const float inv = OPT ? *o.inv_cnt : invT;
   const bool tail = OPT && wid == 0 && lane < rem;
   if (tail) tail_sh[lane] = __uint_as_float((uint32_t)logits[row * V + 8 * nfull + lane] << 16);
+  if constexpr (STATS)
+    for (int i = tid; i < 3 * TABW; i += CP_NT) tab[i] = i < TABW ? -INFINITY : 0.f;
+
+  // CE_STATS: fold a group of 64 consecutive vectors [fv, fv + 64) (lane l
+  // holds vector fv + l when `on`) into the per-shard tables.  Shards hold
+  // vps >= 64 vectors, so at most two shards meet in a group.  A wave keeps
+  // one running value for its current shard cs and reduces it (DPP) into its
+  // table row when the shard changes; a group that straddles two shards is
+  // reduced once per shard.
+  const int wid_u = __builtin_amdgcn_readfirstlane(wid);
+  auto shard_flush = [&](auto max_, float r, int c, float* t) {
+    constexpr bool MX = decltype(max_)::value;
+    if (c < 0) return;
+    const float w = MX ? wave_max(r) : wave_sum(r);
+    if (lane == 0) t[wid_u * CE_PMAX + c] = MX ? fmaxf(t[wid_u * CE_PMAX + c], w) : t[wid_u * CE_PMAX + c] + w;
+  };
+  auto shard_acc = [&](auto max_, float x, bool on, int fv, float& run, int& cs, float* t) {
+    constexpr bool MX = decltype(max_)::value;
+    const float id = MX ? -INFINITY : 0.f;
+    const int lastv = fv + 63 < nvec - 1 ? fv + 63 : nvec - 1;
+    const int sa = (int)__umulhi((uint32_t)fv, o.vps_magic), sb = (int)__umulhi((uint32_t)lastv, o.vps_magic);
+    const float xv = on ? x : id;
+    if (sa == sb) {
+      if (sa != cs) {
+        shard_flush(max_, run, cs, t);
+        run = id;
+        cs = sa;
+      }
+      run = MX ? fmaxf(run, xv) : run + xv;
+    } else {
+      shard_flush(max_, run, cs, t);
+      run = id;
+      cs = -1;
+      const bool in_b = fv + lane >= sb * o.vps;
+      shard_flush(max_, in_b ? id : xv, sa, t);
+      shard_flush(max_, in_b ? xv : id, sb, t);
+    }
+  };
+  using MaxOp = std::integral_constant<bool, true>;
+  using SumOp = std::integral_constant<bool, false>;
+  float* const tabM = tab;
+  float* const tabA = tab + (STATS ? TABW : 0);
+  float* const tabB = tab + (STATS ? 2 * TABW : 0);
+  const int nli = (nlds + CP_NT - 1) / CP_NT;  // LDS-part groups per thread
 
   // Loads, in issue order: register slots [0, CP_RA), the LDS part, register
   // slots [CP_RA, CP_RS).  Slot s of thread tid holds vector s * CP_NT + tid;
@@ -368,10 +425,30 @@ __global__ __launch_bounds__(CP_NT) __attribute__((amdgpu_waves_per_eu(4, 4))) v
 
   // ---- part A: maximum, then exp(z - m_A) once per logit (fp16, in place)
   float run = tail ? tail_sh[lane] : -INFINITY;
+  if constexpr (STATS) {  // the same, with per-shard maxima of part A
+    float r = -INFINITY;
+    int cs = -1;
 #pragma unroll
-  for (int s = 0; s < CP_RA; ++s)
-    if (s * CP_NT + tid < nreg) run = fmaxf(run, vec_max(v[s]));
-  for (int j = tid; j < nlds; j += CP_NT) run = fmaxf(run, vec_max(part[j]));
+    for (int s = 0; s < CP_RA; ++s) {
+      const bool on = s * CP_NT + tid < nreg;
+      const float x = on ? vec_max(v[s]) : -INFINITY;
+      run = fmaxf(run, x);
+      const int fv = s * CP_NT + 64 * wid_u;
+      if (fv < nvec) shard_acc(MaxOp{}, x, on, fv, r, cs, tabM);
+    }
+    for (int i = 0; i < nli; ++i) {
+      const int j = i * CP_NT + tid, fv = nreg + i * CP_NT + 64 * wid_u;
+      const float x = j < nlds ? vec_max(part[j]) : -INFINITY;
+      run = fmaxf(run, x);
+      if (fv < nvec) shard_acc(MaxOp{}, x, j < nlds, fv, r, cs, tabM);
+    }
+    shard_flush(MaxOp{}, r, cs, tabM);
+  } else {
+#pragma unroll
+    for (int s = 0; s < CP_RA; ++s)
+      if (s * CP_NT + tid < nreg) run = fmaxf(run, vec_max(v[s]));
+    for (int j = tid; j < nlds; j += CP_NT) run = fmaxf(run, vec_max(part[j]));
+  }
   {
     const float w = wave_max(run);
     if (lane == 0) red_a[wid] = w;
@@ -408,23 +485,64 @@ __global__ __launch_bounds__(CP_NT) __attribute__((amdgpu_waves_per_eu(4, 4))) v
     }
     // (the scheduling fences keep the compiler from overlapping slots, which
     // would need registers the 88 data registers leave no room for)
+    if constexpr (STATS) {  // the same, with per-shard part A sums
+      float r = 0.f;
+      int cs = -1;
 #pragma unroll
-    for (int s = 0; s < CP_RA; ++s) {
-      if (s * CP_NT + t2 < nreg) expv(v[s], mAL, sumA);
-      __builtin_amdgcn_sched_barrier(0);
-    }
-    for (int j = tid; j < nlds; j += CP_NT) {
-      u32x4 x = part[j];
-      expv(x, mAL, sumA);
-      part[j] = x;  // the same thread reads it back in the gradient pass
+      for (int s = 0; s < CP_RA; ++s) {
+        const bool on = s * CP_NT + t2 < nreg;
+        float vs = 0.f;
+        if (on) expv(v[s], mAL, vs);
+        sumA += vs;
+        const int fv = s * CP_NT + 64 * wid_u;
+        if (fv < nvec) shard_acc(SumOp{}, vs, on, fv, r, cs, tabA);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      for (int i = 0; i < nli; ++i) {
+        const int j = i * CP_NT + tid, fv = nreg + i * CP_NT + 64 * wid_u;
+        float vs = 0.f;
+        if (j < nlds) {
+          u32x4 x = part[j];
+          expv(x, mAL, vs);
+          part[j] = x;
+        }
+        sumA += vs;
+        if (fv < nvec) shard_acc(SumOp{}, vs, j < nlds, fv, r, cs, tabA);
+      }
+      shard_flush(SumOp{}, r, cs, tabA);
+    } else {
+#pragma unroll
+      for (int s = 0; s < CP_RA; ++s) {
+        if (s * CP_NT + t2 < nreg) expv(v[s], mAL, sumA);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      for (int j = tid; j < nlds; j += CP_NT) {
+        u32x4 x = part[j];
+        expv(x, mAL, sumA);
+        part[j] = x;  // the same thread reads it back in the gradient pass
+      }
     }
   }
 
   // ---- part B: the row maximum m, then exp(z - m)
   run = -INFINITY;
+  if constexpr (STATS) {  // the same, with per-shard maxima of part B
+    float r = -INFINITY;
+    int cs = -1;
 #pragma unroll
-  for (int s = CP_RA; s < CP_RS; ++s)
-    if (s * CP_NT + t2 < nreg) run = fmaxf(run, vec_max(v[s]));
+    for (int s = CP_RA; s < CP_RS; ++s) {
+      const bool on = s * CP_NT + t2 < nreg;
+      const float x = on ? vec_max(v[s]) : -INFINITY;
+      run = fmaxf(run, x);
+      const int fv = s * CP_NT + 64 * wid_u;
+      if (fv < nvec) shard_acc(MaxOp{}, x, on, fv, r, cs, tabM);
+    }
+    shard_flush(MaxOp{}, r, cs, tabM);
+  } else {
+#pragma unroll
+    for (int s = CP_RA; s < CP_RS; ++s)
+      if (s * CP_NT + t2 < nreg) run = fmaxf(run, vec_max(v[s]));
+  }
   {
     const float w = wave_max(run);
     if (lane == 0) red_b[wid] = w;
@@ -436,10 +554,26 @@ __global__ __launch_bounds__(CP_NT) __attribute__((amdgpu_waves_per_eu(4, 4))) v
   const float fA = __builtin_amdgcn_exp2f((mA - m) * LOG2E);  // part A's values times fA are exp(z - m)
 #pragma unroll
   for (int s = CP_RA; s < CP_RS; ++s) asm volatile("" : "+v"(v[s]));
+  if constexpr (STATS) {  // the same, with per-shard part B sums
+    float r = 0.f;
+    int cs = -1;
 #pragma unroll
-  for (int s = CP_RA; s < CP_RS; ++s) {
-    if (s * CP_NT + t2 < nreg) expv(v[s], mL, sumB);
-    __builtin_amdgcn_sched_barrier(0);
+    for (int s = CP_RA; s < CP_RS; ++s) {
+      const bool on = s * CP_NT + t2 < nreg;
+      float vs = 0.f;
+      if (on) expv(v[s], mL, vs);
+      sumB += vs;
+      const int fv = s * CP_NT + 64 * wid_u;
+      if (fv < nvec) shard_acc(SumOp{}, vs, on, fv, r, cs, tabB);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    shard_flush(SumOp{}, r, cs, tabB);
+  } else {
+#pragma unroll
+    for (int s = CP_RA; s < CP_RS; ++s) {
+      if (s * CP_NT + t2 < nreg) expv(v[s], mL, sumB);
+      __builtin_amdgcn_sched_barrier(0);
+    }
   }
 
   // exp(z - m) is fp16 in place; the row's values sum to s.
@@ -460,6 +594,20 @@ __global__ __launch_bounds__(CP_NT) __attribute__((amdgpu_waves_per_eu(4, 4))) v
   float zsum = 0.f;
   if constexpr (SMOOTH)
     for (int w = 0; w < CP_NW; ++w) zsum += red_z[w];
+  if constexpr (STATS) {  // (m_r, s_r, t_r) per shard; part A sums rescaled by fA
+    if (tid < o.P) {
+      float mr = -INFINITY, sa = 0.f, sb = 0.f;
+      for (int w = 0; w < CP_NW; ++w) {
+        mr = fmaxf(mr, tabM[w * CE_PMAX + tid]);
+        sa += tabA[w * CE_PMAX + tid];
+        sb += tabB[w * CE_PMAX + tid];
+      }
+      float* st = o.stats + (row * o.P + tid) * 3;
+      st[0] = mr;
+      st[1] = sa * fA + sb;
+      st[2] = (y_ok && y / (8 * (int64_t)o.vps) == tid) ? zy - m : 0.f;
+    }
+  }
   const float eps = SMOOTH ? o.eps : 0.f;
   if (tid == 0)
     row_loss[row] =
@@ -705,7 +853,23 @@ hipError_t launch_vocab_ce(const CeArgs& a, hipStream_t s) {
                       aligned16(a.dlogits) && (nlds + 63) / 64 * 64 <= CP_LDS_VEC;
     const uint16_t* zb = static_cast<const uint16_t*>(a.logits);
     uint16_t* db = static_cast<uint16_t*>(a.dlogits);
-    if (pair) {
+    // With per-shard statistics the paired kernel needs equal shards of whole
+    // 8-logit vectors, at least 64 of them (a wave's group of 64 consecutive
+    // vectors then meets at most two shards), and at most CE_PMAX shards.
+    const int64_t vps = a.parts > 0 ? nvec / a.parts : 0;
+    const bool pair_stats = a.dtype == 1 && a.shard_stats != nullptr && !a.opt && a.V % 8 == 0 &&
+                            a.parts <= CE_PMAX && nvec % a.parts == 0 && vps >= 64 && nvec < 65536 &&
+                            aligned16(a.logits) &&
+                            aligned16(a.dlogits) && (nlds + 63) / 64 * 64 <= CP_LDS_VEC &&
+                            !(getenv("TPRANK_CE_STATS_PATH") && strcmp(getenv("TPRANK_CE_STATS_PATH"), "onerow") == 0);
+    if (pair_stats) {
+      o.stats = a.shard_stats;
+      o.P = a.parts;
+      o.vps = (int)vps;
+      o.vps_magic = 0xffffffffu / (uint32_t)vps + 1u;
+      hipLaunchKernelGGL(ce_pair_kernel<CE_STATS>, dim3((unsigned)a.T), dim3(CP_NT), 0, s, zb, a.labels, db,
+                         a.row_loss, a.V, invT, o);
+    } else if (pair) {
       if (!a.opt)
         hipLaunchKernelGGL(ce_pair_kernel<CE_PLAIN>, dim3((unsigned)a.T), dim3(CP_NT), 0, s, zb, a.labels, db,
                            a.row_loss, a.V, invT, o);

@@ -311,6 +311,35 @@ def test_ce_bf16_row_split_edges(tpr, V):
     assert rel_err(f64(dl), wg) <= TOL_BF16
 
 
+# Per-shard statistics in the paired kernel: equal shards of >= 64 vectors of
+# 8 logits, boundaries inside a wave's group of 64 vectors (vps not a
+# multiple of 64), rows with and without an LDS part, 1 to 16 shards; checked
+# against the oracle, and against the one-row (or three-pass) kernel on the
+# same inputs.
+@pytest.mark.parametrize("vps,parts", [(64, 1), (64, 3), (100, 5), (700, 7), (2004, 8), (1500, 10), (1000, 16)])
+def test_ce_bf16_shard_stats_paired(tpr, vps, parts, monkeypatch):
+    V, T = 8 * vps * parts, 6
+    say("vocab CE bf16 with shard stats, paired kernel: V =", V, "parts =", parts)
+    logits, labels = workloads.vocab_ce(T=T, V=V, seed=vps + parts, device=DEV)
+    labels[0], labels[1], labels[2] = V - 1, 0, min(8 * vps, V - 1)  # last column; first column of shard 1
+    monkeypatch.delenv("TPRANK_CE_STATS_PATH", raising=False)
+    loss, dl, st = tpr.vocab_parallel_ce_fwd_bwd(parts, logits, labels, shard_stats=True)
+    monkeypatch.setenv("TPRANK_CE_STATS_PATH", "onerow")
+    loss1, dl1, st1 = tpr.vocab_parallel_ce_fwd_bwd(parts, logits, labels, shard_stats=True)
+    torch.cuda.synchronize()
+    z, y = f64(logits), labels.cpu().numpy()
+    wl, _, wg, wst = oracle.vocab_parallel_ce(z, y, parts)
+    assert abs(loss.item() - wl) <= 1e-5 * abs(wl)
+    assert rel_err(f64(dl), wg) <= TOL_BF16
+    gst = f64(st)
+    np.testing.assert_array_equal(gst[:, :, 0], wst[:, :, 0])           # maxima are exact
+    np.testing.assert_allclose(gst[:, :, 1], wst[:, :, 1], rtol=1e-5, atol=1e-30)
+    np.testing.assert_allclose(gst[:, :, 2], wst[:, :, 2], rtol=1e-6, atol=1e-6)
+    np.testing.assert_array_equal(gst[:, :, 0], f64(st1)[:, :, 0])
+    np.testing.assert_allclose(gst[:, :, 1], f64(st1)[:, :, 1], rtol=1e-5)
+    assert abs(loss.item() - loss1.item()) <= 1e-5 * abs(loss1.item())
+
+
 def test_ce_zero_rows(tpr):
     say("vocab CE T=0")
     logits = torch.empty(0, 16, dtype=torch.bfloat16, device=DEV)
@@ -369,6 +398,10 @@ def test_determinism(tpr):
     a = tpr.vocab_parallel_ce_fwd_bwd(8, logits, labels)
     b = tpr.vocab_parallel_ce_fwd_bwd(8, logits, labels)
     assert torch.equal(a[0], b[0]) and torch.equal(a[1], b[1])
+    a = tpr.vocab_parallel_ce_fwd_bwd(8, logits, labels, shard_stats=True)
+    b = tpr.vocab_parallel_ce_fwd_bwd(8, logits, labels, shard_stats=True)
+    for p, q in zip(a, b):
+        assert torch.equal(p, q)
     x, w1, w2, gy = workloads.rank_mlp(300, 264, 200, seed=4, device=DEV)
     r1 = tpr.tp_mlp_fwd_bwd(3, x, w1, w2, gy)
     r2 = tpr.tp_mlp_fwd_bwd(3, x, w1, w2, gy)
