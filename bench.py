@@ -78,6 +78,10 @@ def stored_traffic(kernel, path=TRAFFIC_JSON):
 GEMM_KERNEL = "gemm_bf16_dma_kernel"
 CE_KERNEL = "ce_pair_kernel"
 COPY_KERNEL = "neg_kernel"
+# Kernel-name patterns for the counter rows: every launch of the GEMM kernel,
+# and the CE kernel's plain instance (the one the bench's CE call runs; the
+# per-shard-statistics instance ce_pair_kernel<3> is another workload).
+TRAFFIC_MATCH = {GEMM_KERNEL: GEMM_KERNEL, CE_KERNEL: CE_KERNEL + "<0>"}
 
 
 def traffic_from(fetch_csv, write_csv, copy_bytes, out_path=TRAFFIC_JSON):
@@ -107,7 +111,7 @@ def traffic_from(fetch_csv, write_csv, copy_bytes, out_path=TRAFFIC_JSON):
         scale = copy_bytes / (copy[0] * 1024.0)
         out[counter] = {"copy_kib": copy[0], "scale": scale}
         for kernel in (GEMM_KERNEL, CE_KERNEL):
-            vals = [v * 1024.0 * scale for n, v in rows if kernel in n]
+            vals = [v * 1024.0 * scale for n, v in rows if TRAFFIC_MATCH[kernel] in n]
             out[counter][kernel] = {"launches": len(vals), "avg_bytes": sum(vals) / max(len(vals), 1)}
     for kernel in (GEMM_KERNEL, CE_KERNEL):
         out[kernel + "_bytes_per_launch"] = (out["FETCH_SIZE"][kernel]["avg_bytes"] +
