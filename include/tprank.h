@@ -32,6 +32,11 @@
  *     of 8) selects the vectorised kernels, anything else the element-wise
  *     ones.  Results do not depend on which is chosen beyond fp32 rounding
  *     order.
+ *   - Two environment variables select fallback kernels on the same inputs
+ *     (the tests use them to cover those kernels): TPRANK_GEMM_PATH=staged
+ *     sends every bf16 product to the register-staged GEMM, and
+ *     TPRANK_CE_STATS_PATH=onerow computes a requested shard_stats output
+ *     with the one-row-per-workgroup CE kernel.
  */
 #ifndef TPRANK_H
 #define TPRANK_H
