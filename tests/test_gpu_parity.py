@@ -176,6 +176,30 @@ def test_inner_gemm_70b_rank_sampled(tpr):
     assert torch.equal(dA8, dA) and torch.equal(dB8, dB)
 
 
+@pytest.mark.parametrize("K", [32736, 32768])
+def test_bf16_gemm_operand_size_limit(tpr, K):
+    # The direct-to-LDS kernel addresses each operand with 32-bit byte offsets
+    # and takes operands below 1 GiB: at M = 16384 an A of K = 32736 columns
+    # (1023 MiB, K a multiple of 32) runs there with its largest offsets in
+    # every product, K = 32768 (1 GiB) sends the products reading A to the
+    # register-staged kernel.  Both checked on sampled rows and columns.
+    M, N = 16384, 64
+    say("bf16 inner GEMM at the 1 GiB operand limit: M, K, N =", M, K, N)
+    a, b, g = workloads.inner_gemm(M, K, N, seed=K, device=DEV)
+    Y, dA, dB = tpr.sharded_matmul_fwd_bwd("inner", 1, a, b, g)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(K)
+    rows = np.sort(np.concatenate([rng.choice(M, 6, replace=False), [0, M - 1]]))
+    krows = np.sort(np.concatenate([rng.choice(K, 6, replace=False), [0, K - 1]]))
+    ri, ki = torch.from_numpy(rows).to(DEV), torch.from_numpy(krows).to(DEV)
+    B, G = f64(b), f64(g)
+    assert rel_err(f64(Y[ri]), f64(a[ri]) @ B) <= 1e-4
+    assert rel_err(f64(dA[ri]), f64(g[ri]) @ B.T) <= 1e-4
+    assert rel_err(f64(dB[ki]), f64(a[:, ki]).T @ G) <= 1e-4
+    del Y, dA, dB, a, b, g
+    torch.cuda.empty_cache()
+
+
 # ---------------------------------------------------------------- TP MLP
 
 def test_mlp_lesson_selftest_fp32(tpr):
