@@ -16,7 +16,9 @@ library launches on.  After the timed steps, torch's copy_ of the logits (the
 CE's bytes, read once and written once) is timed as the copy-rate context of
 the CE figure (``roofline_ce.copy_same_bytes_gbs``), and the MLP's six
 products through torch.mm (hipBLASLt) as library context
-(``mlp_gemms_via_torch_mm``).
+(``mlp_gemms_via_torch_mm``).  The cross-rank partial sum is timed on its own
+through tprank_partial_sum (``roofline_reduce``: 8 fp32 partials of the
+inner split's 8192 x 8192 Y, (8 + 1) * 4 bytes per output element).
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline] [--copy-runs N] [--blas-runs N]
                        [--copy-bytes N]
@@ -47,6 +49,7 @@ MLP_8B = dict(T=4096, d=4096, f=1792)
 ATTN = dict(T=8192, d=8192, n_q_heads=8, n_kv_heads=1, head_dim=128)
 GATED = dict(T=8192, d=8192, f=3584, act="silu")
 CE_OPTS = dict(T=4096, V=128256, v_valid=128000, parts=8, label_smoothing=0.1, ignore_frac=0.125)
+REDUCE = dict(slots=8, M=8192, N=8192)
 
 
 def kernel_source_digest():
@@ -77,11 +80,12 @@ def stored_traffic(kernel, path=TRAFFIC_JSON):
 
 GEMM_KERNEL = "gemm_bf16_dma_kernel"
 CE_KERNEL = "ce_pair_kernel"
+REDUCE_KERNEL = "reduce_vec4_kernel"
 COPY_KERNEL = "neg_kernel"
 # Kernel-name patterns for the counter rows: every launch of the GEMM kernel,
 # and the CE kernel's plain instance (the one the bench's CE call runs; the
 # per-shard-statistics instance ce_pair_kernel<3> is another workload).
-TRAFFIC_MATCH = {GEMM_KERNEL: GEMM_KERNEL, CE_KERNEL: CE_KERNEL + "<0>"}
+TRAFFIC_MATCH = {GEMM_KERNEL: GEMM_KERNEL, CE_KERNEL: CE_KERNEL + "<0>", REDUCE_KERNEL: REDUCE_KERNEL + "<8>"}
 
 
 def traffic_from(fetch_csv, write_csv, copy_bytes, out_path=TRAFFIC_JSON):
@@ -110,10 +114,12 @@ def traffic_from(fetch_csv, write_csv, copy_bytes, out_path=TRAFFIC_JSON):
             raise SystemExit(f"{path}: expected one {COPY_KERNEL} dispatch, found {len(copy)}")
         scale = copy_bytes / (copy[0] * 1024.0)
         out[counter] = {"copy_kib": copy[0], "scale": scale}
-        for kernel in (GEMM_KERNEL, CE_KERNEL):
+        for kernel in (GEMM_KERNEL, CE_KERNEL, REDUCE_KERNEL):
             vals = [v * 1024.0 * scale for n, v in rows if TRAFFIC_MATCH[kernel] in n]
             out[counter][kernel] = {"launches": len(vals), "avg_bytes": sum(vals) / max(len(vals), 1)}
-    for kernel in (GEMM_KERNEL, CE_KERNEL):
+    for kernel in (GEMM_KERNEL, CE_KERNEL, REDUCE_KERNEL):
+        if out["FETCH_SIZE"][kernel]["launches"] == 0:
+            continue
         out[kernel + "_bytes_per_launch"] = (out["FETCH_SIZE"][kernel]["avg_bytes"] +
                                              out["WRITE_SIZE"][kernel]["avg_bytes"])
     with open(out_path, "w") as f:
@@ -384,6 +390,41 @@ def bench_ce_opts(tpr, workloads, dev, steps):
             "bytes_per_call": nbytes}
 
 
+def bench_reduce(tpr, dev, steps):
+    """The cross-rank partial sum on its own (tprank_partial_sum): the
+    70B rank's inner-axis split over 8 ranks leaves 8 fp32 partials of
+    Y (8192 x 8192) to be summed.  Algorithmic bytes: (8 + 1) * 4 per output
+    element (each partial read once, the sum written once)."""
+    import torch
+
+    P, n = REDUCE["slots"], REDUCE["M"] * REDUCE["N"]
+    g = torch.Generator(device=dev)
+    g.manual_seed(14)
+    parts = torch.randn(P, n, generator=g, device=dev)
+    out = torch.empty(n, device=dev)
+    for _ in range(2):
+        tpr.partial_sum(parts, out=out)
+    torch.cuda.synchronize()
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(steps)]
+    for e in ev:
+        e[0].record()
+        tpr.partial_sum(parts, out=out)
+        e[1].record()
+    torch.cuda.synchronize()
+    ms = sorted(e[0].elapsed_time(e[1]) for e in ev)
+    nbytes = (P + 1) * 4.0 * n
+    mean = sum(ms) / len(ms)
+    gbs = nbytes / (mean * 1e-3) / 1e9
+    del parts, out
+    torch.cuda.empty_cache()
+    return {"kernel": f"reduce_vec4_kernel<{P}> (one launch per call)", "bound": "hbm",
+            "workload": f"{P} fp32 partials of the inner-split Y, {REDUCE['M']} x {REDUCE['N']}",
+            "steps": steps, "bytes_per_launch": nbytes, "avg_launch_us": round(mean * 1e3, 2),
+            "min_launch_us": round(ms[0] * 1e3, 2), "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS,
+            "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4),
+            "traffic": stored_traffic(REDUCE_KERNEL + "_bytes_per_launch")}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -402,6 +443,8 @@ def main():
                     help="timed calls of the gated SiLU MLP at the 70B rank size (reported beside the step; 0 = skip)")
     ap.add_argument("--attn-steps", type=int, default=10,
                     help="timed calls of the 70B-rank attention projections (reported beside the step; 0 = skip)")
+    ap.add_argument("--reduce-steps", type=int, default=20,
+                    help="timed calls of the cross-rank partial sum (8 x 8192 x 8192 fp32; 0 = skip)")
     ap.add_argument("--small-runs", type=int, default=100,
                     help="timed calls per small (latency-bound) configuration and of the CE (0 = skip)")
     ap.add_argument("--traffic-from", nargs=3, metavar=("FETCH_CSV", "WRITE_CSV", "COPY_BYTES"))
@@ -564,6 +607,9 @@ def main():
     ce_stats = None
     if args.ce_stats_steps > 0:
         ce_stats = bench_ce_stats(tpr, workloads, dev, args.ce_stats_steps)
+    reduce = None
+    if args.reduce_steps > 0:
+        reduce = bench_reduce(tpr, dev, args.reduce_steps)
     ce_opts = None
     if args.ce_opts_steps > 0:
         ce_opts = bench_ce_opts(tpr, workloads, dev, args.ce_opts_steps)
@@ -627,6 +673,7 @@ def main():
             "copy_same_bytes_gbs": None if copy_gbs is None else round(copy_gbs, 1),
             "frac_of_copy": None if copy_gbs is None else round(ce_gbs / copy_gbs, 4),
         },
+        "roofline_reduce": reduce,
         "kernel_source_digest": kernel_source_digest(),
     }
     if head is not None:

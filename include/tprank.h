@@ -118,6 +118,28 @@ int sharded_matmul_fwd_bwd(int axis, int parts, int dtype, int64_t M, int64_t K,
                            float* Y, float* dA, float* dB,
                            void* ws, size_t ws_bytes, void* stream);
 
+/* ---- cross-rank partial sum -------------------------------------------- */
+/*
+ * The sum a split leaves behind, as the simulated all-reduce(sum) on one GPU:
+ * [GEMM] 复杂度 and 解题路线 steps 2-4 (dB for a row split, dA for a column
+ * split, Y for an inner split), [TP] 2.A step 5 and [CARDS] 02 / BACKWARD
+ * (the MLP's y and dx).  The entry points above run it on their own
+ * partials; this call exposes it on caller-provided ones:
+ *     out[i] = partials[i] + partials[slot_stride + i] + ...
+ *              + partials[(nslots - 1) * slot_stride + i],
+ * added in slot (rank) order in fp32, so every call gives the same bits.
+ *   partials: nslots fp32 slots of n elements, slot s at element offset
+ *   s * slot_stride (slot_stride >= n);  out: n fp32 elements, not
+ *   overlapping the partials.  n == 0 enqueues nothing; nslots == 0 writes
+ *   zeros (the empty sum).  One HBM pass: (nslots + 1) * 4 bytes move per
+ *   output element.
+ * Errors: SHAPE (n < 0, nslots < 0 or slot_stride < n), NULLPTR (out, or
+ * partials when nslots > 0, NULL with n > 0), VALUE (out overlaps the
+ * partials), HIP.
+ */
+int tprank_partial_sum(int nslots, int64_t n, const float* partials, int64_t slot_stride, float* out,
+                       void* stream);
+
 /* ---- column-then-row tensor-parallel GELU MLP ------------------------- */
 /*
  * Bytes of workspace tp_mlp_fwd_bwd() needs: gelu' of the pre-activation
@@ -335,6 +357,10 @@ size_t vocab_parallel_head_ce_workspace_bytes(int parts, int dtype, int64_t T, i
  *   labels: T int64 with 0 <= y < V (same contract as the CE entry point);
  *   loss: one fp32 on the device;  dh: fp32 T x d;  dw: fp32, same shape and
  *   layout as w.  T == 0 writes loss = 0 and zeroes dw.
+ *   On return the workspace holds the logits (T x V in `dtype`, row-major)
+ *   from its first byte and dlogits (T x V in `dtype`) from the next
+ *   multiple of 256 bytes after them; the caller may read both once the
+ *   stream has completed the call.
  * Errors: SHAPE, PARTITION, DTYPE (dtype or w_layout), NULLPTR, WORKSPACE, HIP.
  */
 int vocab_parallel_head_ce_fwd_bwd(int parts, int dtype, int w_layout, int64_t T, int64_t d, int64_t V,

@@ -9,7 +9,7 @@ ignore index and label smoothing), alone or behind the vocabulary-parallel
 output head.  All compute runs in the library's HIP
 kernels; torch provides device memory and streams.
 """
-from .binding import (ACTS, AXES, DTYPES, LIB_PATH, W_LAYOUTS, TprError, load_library, shard_range,
+from .binding import (ACTS, AXES, DTYPES, LIB_PATH, W_LAYOUTS, TprError, load_library, partial_sum, shard_range,
                       sharded_matmul_fwd_bwd, sharded_matmul_workspace_bytes, tp_mlp_fwd_bwd,
                       tp_mlp_workspace_bytes, tp_mlp_act_fwd_bwd, tp_mlp_act_workspace_bytes,
                       tp_attn_proj_fwd_bwd, tp_attn_proj_workspace_bytes,
@@ -18,7 +18,7 @@ from .binding import (ACTS, AXES, DTYPES, LIB_PATH, W_LAYOUTS, TprError, load_li
                       vocab_parallel_head_ce_fwd_bwd, vocab_parallel_head_ce_workspace_bytes)
 
 __all__ = [
-    "ACTS", "AXES", "DTYPES", "LIB_PATH", "W_LAYOUTS", "TprError", "load_library", "shard_range",
+    "ACTS", "AXES", "DTYPES", "LIB_PATH", "W_LAYOUTS", "TprError", "load_library", "partial_sum", "shard_range",
     "sharded_matmul_fwd_bwd", "sharded_matmul_workspace_bytes", "tp_mlp_fwd_bwd", "tp_mlp_workspace_bytes",
     "tp_mlp_act_fwd_bwd", "tp_mlp_act_workspace_bytes",
     "tp_attn_proj_fwd_bwd", "tp_attn_proj_workspace_bytes",

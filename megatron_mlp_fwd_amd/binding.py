@@ -3,7 +3,8 @@
 Argument marshalling only: checks that tensors live on the GPU, are
 contiguous and have the shapes and dtypes the C ABI expects (the library
 cannot see buffer sizes), allocates outputs and the workspace with torch's
-caching allocator, and passes raw device pointers plus the current HIP stream.
+caching allocator on the stream the call launches on (``stream``, else the
+current stream), and passes raw device pointers plus that HIP stream.
 Every step of the computation runs in the library's HIP kernels; there is no
 fallback of any kind -- if the library is missing, loading fails.
 """
@@ -44,6 +45,7 @@ _SIGS = {
     "vocab_parallel_head_ce_workspace_bytes": (_sz, [_i32, _i32, _i64, _i64, _i64]),
     "vocab_parallel_head_ce_fwd_bwd": (_i32, [_i32, _i32, _i32, _i64, _i64, _i64, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
                                               _sz, _vp]),
+    "tprank_partial_sum": (_i32, [_i32, _i64, _vp, _i64, _vp, _vp]),
     "tprank_last_error": (ctypes.c_char_p, []),
 }
 
@@ -80,9 +82,35 @@ def _ptr(t):
     return None if t is None or t.numel() == 0 else t.data_ptr()
 
 
-def _stream(stream):
-    s = stream if stream is not None else torch.cuda.current_stream()
-    return s.cuda_stream
+class _On:
+    """Device and stream of one call.  Outputs and the workspace that the
+    binding allocates are allocated on the stream the kernels are launched
+    on: torch's caching allocator hands a freed block only to later
+    allocations on the stream it was allocated on, so a workspace dropped
+    when the call returns cannot be reused by another stream while the
+    call's kernels still run on this one."""
+
+    def __init__(self, device, stream):
+        self.device = device
+        with torch.cuda.device(device):
+            self.stream = stream if stream is not None else torch.cuda.current_stream()
+        self._ctx = None
+
+    def __enter__(self):
+        self._dev = torch.cuda.device(self.device)
+        self._dev.__enter__()
+        self._ctx = torch.cuda.stream(self.stream)
+        self._ctx.__enter__()
+        return self
+
+    def __exit__(self, *exc):
+        self._ctx.__exit__(*exc)
+        self._dev.__exit__(*exc)
+        return False
+
+    @property
+    def handle(self):
+        return self.stream.cuda_stream
 
 
 def _need(t, name, shape, dtype, device):
@@ -138,17 +166,39 @@ def sharded_matmul_fwd_bwd(axis, parts, A, B, G, out=None, workspace=None, strea
     _need(A, "A", (M, K), dt, dev)
     _need(B, "B", (K, N), dt, dev)
     _need(G, "G", (M, N), dt, dev)
-    if out is None:
-        out = (torch.empty(M, N, device=dev), torch.empty(M, K, device=dev), torch.empty(K, N, device=dev))
-    Y, dA, dB = out
-    _need(Y, "Y", (M, N), torch.float32, dev)
-    _need(dA, "dA", (M, K), torch.float32, dev)
-    _need(dB, "dB", (K, N), torch.float32, dev)
-    ws, wsb = _workspace(lib.sharded_matmul_workspace_bytes(ax, parts, DTYPES[dt], M, K, N), dev, workspace)
-    with torch.cuda.device(dev):
+    with _On(dev, stream) as on:
+        if out is None:
+            out = (torch.empty(M, N, device=dev), torch.empty(M, K, device=dev), torch.empty(K, N, device=dev))
+        Y, dA, dB = out
+        _need(Y, "Y", (M, N), torch.float32, dev)
+        _need(dA, "dA", (M, K), torch.float32, dev)
+        _need(dB, "dB", (K, N), torch.float32, dev)
+        ws, wsb = _workspace(lib.sharded_matmul_workspace_bytes(ax, parts, DTYPES[dt], M, K, N), dev, workspace)
         _check(lib.sharded_matmul_fwd_bwd(ax, parts, DTYPES[dt], M, K, N, _ptr(A), _ptr(B), _ptr(G), _ptr(Y),
-                                          _ptr(dA), _ptr(dB), _ptr(ws), wsb, _stream(stream)))
+                                          _ptr(dA), _ptr(dB), _ptr(ws), wsb, on.handle))
     return Y, dA, dB
+
+
+def partial_sum(partials, out=None, stream=None):
+    """Sum of the fp32 slots ``partials[0] + partials[1] + ...`` (the first
+    dimension indexes the simulated ranks), added in slot order.  Returns
+    ``out`` (shaped like one slot)."""
+    lib = load_library()
+    if partials.dim() < 1:
+        raise ValueError("partials must have a slot dimension")
+    nslots = partials.shape[0]
+    shape = tuple(partials.shape[1:])
+    dev = partials.device
+    _need(partials, "partials", tuple(partials.shape), torch.float32, dev)
+    n = 1
+    for k in shape:
+        n *= k
+    with _On(dev, stream) as on:
+        if out is None:
+            out = torch.empty(shape, device=dev)
+        _need(out, "out", shape, torch.float32, dev)
+        _check(lib.tprank_partial_sum(nslots, n, _ptr(partials), n, _ptr(out), on.handle))
+    return out
 
 
 def tp_mlp_workspace_bytes(tp, dtype, T, d, f):
@@ -180,18 +230,18 @@ def tp_mlp_fwd_bwd(tp, x, w1, w2, gy, w_layout="math", out=None, workspace=None,
     _need(gy, "gy", xs, dt, dev)
     _need(w1, "w1", wshape1, dt, dev)
     _need(w2, "w2", wshape2, dt, dev)
-    if out is None:
-        out = (torch.empty(xs, device=dev), torch.empty(xs, device=dev),
-               torch.empty(wshape1, device=dev), torch.empty(wshape2, device=dev))
-    y, dx, dw1, dw2 = out
-    _need(y, "y", xs, torch.float32, dev)
-    _need(dx, "dx", xs, torch.float32, dev)
-    _need(dw1, "dw1", wshape1, torch.float32, dev)
-    _need(dw2, "dw2", wshape2, torch.float32, dev)
-    ws, wsb = _workspace(lib.tp_mlp_workspace_bytes(tp, DTYPES[dt], T, d, f), dev, workspace)
-    with torch.cuda.device(dev):
+    with _On(dev, stream) as on:
+        if out is None:
+            out = (torch.empty(xs, device=dev), torch.empty(xs, device=dev),
+                   torch.empty(wshape1, device=dev), torch.empty(wshape2, device=dev))
+        y, dx, dw1, dw2 = out
+        _need(y, "y", xs, torch.float32, dev)
+        _need(dx, "dx", xs, torch.float32, dev)
+        _need(dw1, "dw1", wshape1, torch.float32, dev)
+        _need(dw2, "dw2", wshape2, torch.float32, dev)
+        ws, wsb = _workspace(lib.tp_mlp_workspace_bytes(tp, DTYPES[dt], T, d, f), dev, workspace)
         _check(lib.tp_mlp_fwd_bwd(tp, DTYPES[dt], layout, T, d, f, _ptr(x), _ptr(w1), _ptr(w2), _ptr(gy), _ptr(y),
-                                  _ptr(dx), _ptr(dw1), _ptr(dw2), _ptr(ws), wsb, _stream(stream)))
+                                  _ptr(dx), _ptr(dw1), _ptr(dw2), _ptr(ws), wsb, on.handle))
     return y, dx, dw1, dw2
 
 
@@ -230,21 +280,21 @@ def tp_mlp_act_fwd_bwd(tp, x, w1, w2, gy, act="gelu", w3=None, w_layout="math", 
     gated = w3 is not None
     if gated:
         _need(w3, "w3", wshape1, dt, dev)
-    if out is None:
-        out = (torch.empty(xs, device=dev), torch.empty(xs, device=dev), torch.empty(wshape1, device=dev),
-               torch.empty(wshape2, device=dev), torch.empty(wshape1, device=dev) if gated else None)
-    y, dx, dw1, dw2, dw3 = out
-    _need(y, "y", xs, torch.float32, dev)
-    _need(dx, "dx", xs, torch.float32, dev)
-    _need(dw1, "dw1", wshape1, torch.float32, dev)
-    _need(dw2, "dw2", wshape2, torch.float32, dev)
-    if gated:
-        _need(dw3, "dw3", wshape1, torch.float32, dev)
-    ws, wsb = _workspace(lib.tp_mlp_act_workspace_bytes(tp, DTYPES[dt], int(gated), T, d, f), dev, workspace)
-    with torch.cuda.device(dev):
+    with _On(dev, stream) as on:
+        if out is None:
+            out = (torch.empty(xs, device=dev), torch.empty(xs, device=dev), torch.empty(wshape1, device=dev),
+                   torch.empty(wshape2, device=dev), torch.empty(wshape1, device=dev) if gated else None)
+        y, dx, dw1, dw2, dw3 = out
+        _need(y, "y", xs, torch.float32, dev)
+        _need(dx, "dx", xs, torch.float32, dev)
+        _need(dw1, "dw1", wshape1, torch.float32, dev)
+        _need(dw2, "dw2", wshape2, torch.float32, dev)
+        if gated:
+            _need(dw3, "dw3", wshape1, torch.float32, dev)
+        ws, wsb = _workspace(lib.tp_mlp_act_workspace_bytes(tp, DTYPES[dt], int(gated), T, d, f), dev, workspace)
         _check(lib.tp_mlp_act_fwd_bwd(tp, DTYPES[dt], layout, ACTS[act], T, d, f, _ptr(x), _ptr(w1), _ptr(w3),
                                       _ptr(w2), _ptr(gy), _ptr(y), _ptr(dx), _ptr(dw1), _ptr(dw3), _ptr(dw2),
-                                      _ptr(ws), wsb, _stream(stream)))
+                                      _ptr(ws), wsb, on.handle))
     return y, dx, dw1, dw2, dw3
 
 
@@ -278,23 +328,23 @@ def tp_attn_proj_fwd_bwd(tp, x, w_qkv, w_o, ctx, gy, dqkv, n_q_heads, n_kv_heads
     _need(w_o, "w_o", wos, dt, dev)
     _need(ctx, "ctx", (T, nq), dt, dev)
     _need(dqkv, "dqkv", (T, nqkv), dt, dev)
-    if out is None:
-        out = (torch.empty(T, nqkv, dtype=dt, device=dev), torch.empty(T, d, device=dev),
-               torch.empty(T, nq, dtype=dt, device=dev), torch.empty(T, d, device=dev),
-               torch.empty(wqs, device=dev), torch.empty(wos, device=dev))
-    qkv, y, dctx, dx, dwq, dwo = out
-    _need(qkv, "qkv", (T, nqkv), dt, dev)
-    _need(y, "y", (T, d), torch.float32, dev)
-    _need(dctx, "dctx", (T, nq), dt, dev)
-    _need(dx, "dx", (T, d), torch.float32, dev)
-    _need(dwq, "dw_qkv", wqs, torch.float32, dev)
-    _need(dwo, "dw_o", wos, torch.float32, dev)
-    ws, wsb = _workspace(lib.tp_attn_proj_workspace_bytes(tp, DTYPES[dt], T, d, n_q_heads, n_kv_heads, head_dim),
-                         dev, workspace)
-    with torch.cuda.device(dev):
+    with _On(dev, stream) as on:
+        if out is None:
+            out = (torch.empty(T, nqkv, dtype=dt, device=dev), torch.empty(T, d, device=dev),
+                   torch.empty(T, nq, dtype=dt, device=dev), torch.empty(T, d, device=dev),
+                   torch.empty(wqs, device=dev), torch.empty(wos, device=dev))
+        qkv, y, dctx, dx, dwq, dwo = out
+        _need(qkv, "qkv", (T, nqkv), dt, dev)
+        _need(y, "y", (T, d), torch.float32, dev)
+        _need(dctx, "dctx", (T, nq), dt, dev)
+        _need(dx, "dx", (T, d), torch.float32, dev)
+        _need(dwq, "dw_qkv", wqs, torch.float32, dev)
+        _need(dwo, "dw_o", wos, torch.float32, dev)
+        ws, wsb = _workspace(lib.tp_attn_proj_workspace_bytes(tp, DTYPES[dt], T, d, n_q_heads, n_kv_heads, head_dim),
+                             dev, workspace)
         _check(lib.tp_attn_proj_fwd_bwd(tp, DTYPES[dt], layout, T, d, n_q_heads, n_kv_heads, head_dim, _ptr(x),
                                         _ptr(w_qkv), _ptr(w_o), _ptr(ctx), _ptr(gy), _ptr(dqkv), _ptr(qkv), _ptr(y),
-                                        _ptr(dctx), _ptr(dx), _ptr(dwq), _ptr(dwo), _ptr(ws), wsb, _stream(stream)))
+                                        _ptr(dctx), _ptr(dx), _ptr(dwq), _ptr(dwo), _ptr(ws), wsb, on.handle))
     return qkv, y, dctx, dx, dwq, dwo
 
 
@@ -317,18 +367,18 @@ def vocab_parallel_ce_fwd_bwd(parts, logits, labels, shard_stats=False, out=None
     dev = logits.device
     _need(logits, "logits", (T, V), dt, dev)
     _need(labels, "labels", (T,), torch.int64, dev)
-    if out is None:
-        out = (torch.empty((), device=dev), torch.empty(T, V, dtype=dt, device=dev),
-               torch.empty(T, parts, 3, device=dev) if shard_stats else None)
-    loss, dlogits, stats = out
-    _need(loss, "loss", (), torch.float32, dev)
-    _need(dlogits, "dlogits", (T, V), dt, dev)
-    if stats is not None:
-        _need(stats, "shard_stats", (T, parts, 3), torch.float32, dev)
-    ws, wsb = _workspace(lib.vocab_parallel_ce_workspace_bytes(parts, T, V), dev, workspace)
-    with torch.cuda.device(dev):
+    with _On(dev, stream) as on:
+        if out is None:
+            out = (torch.empty((), device=dev), torch.empty(T, V, dtype=dt, device=dev),
+                   torch.empty(T, parts, 3, device=dev) if shard_stats else None)
+        loss, dlogits, stats = out
+        _need(loss, "loss", (), torch.float32, dev)
+        _need(dlogits, "dlogits", (T, V), dt, dev)
+        if stats is not None:
+            _need(stats, "shard_stats", (T, parts, 3), torch.float32, dev)
+        ws, wsb = _workspace(lib.vocab_parallel_ce_workspace_bytes(parts, T, V), dev, workspace)
         _check(lib.vocab_parallel_ce_fwd_bwd(parts, DTYPES[dt], T, V, _ptr(logits), _ptr(labels), loss.data_ptr(),
-                                             _ptr(dlogits), _ptr(stats), _ptr(ws), wsb, _stream(stream)))
+                                             _ptr(dlogits), _ptr(stats), _ptr(ws), wsb, on.handle))
     return loss, dlogits, stats
 
 
@@ -356,19 +406,19 @@ def vocab_parallel_ce_opts_fwd_bwd(parts, logits, labels, v_valid=None, ignore_i
     dev = logits.device
     _need(logits, "logits", (T, V), dt, dev)
     _need(labels, "labels", (T,), torch.int64, dev)
-    if out is None:
-        out = (torch.empty((), device=dev), torch.empty(T, V, dtype=dt, device=dev),
-               torch.empty(T, parts, 3, device=dev) if shard_stats else None)
-    loss, dlogits, stats = out
-    _need(loss, "loss", (), torch.float32, dev)
-    _need(dlogits, "dlogits", (T, V), dt, dev)
-    if stats is not None:
-        _need(stats, "shard_stats", (T, parts, 3), torch.float32, dev)
-    ws, wsb = _workspace(lib.vocab_parallel_ce_opts_workspace_bytes(parts, T, V), dev, workspace)
-    with torch.cuda.device(dev):
+    with _On(dev, stream) as on:
+        if out is None:
+            out = (torch.empty((), device=dev), torch.empty(T, V, dtype=dt, device=dev),
+                   torch.empty(T, parts, 3, device=dev) if shard_stats else None)
+        loss, dlogits, stats = out
+        _need(loss, "loss", (), torch.float32, dev)
+        _need(dlogits, "dlogits", (T, V), dt, dev)
+        if stats is not None:
+            _need(stats, "shard_stats", (T, parts, 3), torch.float32, dev)
+        ws, wsb = _workspace(lib.vocab_parallel_ce_opts_workspace_bytes(parts, T, V), dev, workspace)
         _check(lib.vocab_parallel_ce_opts_fwd_bwd(parts, DTYPES[dt], T, V, vv, ign, float(label_smoothing),
                                                   _ptr(logits), _ptr(labels), loss.data_ptr(), _ptr(dlogits),
-                                                  _ptr(stats), _ptr(ws), wsb, _stream(stream)))
+                                                  _ptr(stats), _ptr(ws), wsb, on.handle))
     return loss, dlogits, stats
 
 
@@ -395,15 +445,15 @@ def vocab_parallel_head_ce_fwd_bwd(parts, h, w, labels, w_layout="math", out=Non
     _need(h, "h", (T, d), dt, dev)
     _need(w, "w", wshape, dt, dev)
     _need(labels, "labels", (T,), torch.int64, dev)
-    if out is None:
-        out = (torch.empty((), device=dev), torch.empty(T, d, device=dev), torch.empty(wshape, device=dev))
-    loss, dh, dw = out
-    _need(loss, "loss", (), torch.float32, dev)
-    _need(dh, "dh", (T, d), torch.float32, dev)
-    _need(dw, "dw", wshape, torch.float32, dev)
-    ws, wsb = _workspace(lib.vocab_parallel_head_ce_workspace_bytes(parts, DTYPES[dt], T, d, V), dev, workspace)
-    with torch.cuda.device(dev):
+    with _On(dev, stream) as on:
+        if out is None:
+            out = (torch.empty((), device=dev), torch.empty(T, d, device=dev), torch.empty(wshape, device=dev))
+        loss, dh, dw = out
+        _need(loss, "loss", (), torch.float32, dev)
+        _need(dh, "dh", (T, d), torch.float32, dev)
+        _need(dw, "dw", wshape, torch.float32, dev)
+        ws, wsb = _workspace(lib.vocab_parallel_head_ce_workspace_bytes(parts, DTYPES[dt], T, d, V), dev, workspace)
         _check(lib.vocab_parallel_head_ce_fwd_bwd(parts, DTYPES[dt], layout, T, d, V, _ptr(h), _ptr(w), _ptr(labels),
                                                   loss.data_ptr(), _ptr(dh), _ptr(dw), _ptr(ws), wsb,
-                                                  _stream(stream)))
+                                                  on.handle))
     return loss, dh, dw

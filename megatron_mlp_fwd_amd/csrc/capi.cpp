@@ -8,11 +8,38 @@
 #include <cstring>
 #include <cstdarg>
 #include <cstdio>
+#include <mutex>
 #include <string>
 #include <vector>
 
 #include "common.h"
 #include "tprank.h"
+
+namespace tpr {
+
+Topology device_topology() {
+  constexpr int kMaxDev = 64;
+  static std::mutex mu;
+  static Topology known[kMaxDev];
+  static bool have[kMaxDev];
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDev) {
+    (void)hipGetLastError();
+    return Topology{256, 8};
+  }
+  std::lock_guard<std::mutex> lock(mu);
+  if (!have[dev]) {
+    int cus = 0, xcds = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0) cus = 256;
+    if (hipDeviceGetAttribute(&xcds, hipDeviceAttributeNumberOfXccs, dev) != hipSuccess || xcds <= 0) xcds = 1;
+    (void)hipGetLastError();
+    known[dev] = Topology{cus, xcds};
+    have[dev] = true;
+  }
+  return known[dev];
+}
+
+}  // namespace tpr
 
 namespace {
 
@@ -226,10 +253,31 @@ int sharded_matmul_fwd_bwd(int axis, int parts, int dtype, int64_t M, int64_t K,
   return TPR_OK;
 }
 
+// ---------------------------------------------------------------- partial sum
+int tprank_partial_sum(int nslots, int64_t n, const float* partials, int64_t slot_stride, float* out,
+                       void* stream) {
+  if (n < 0 || nslots < 0 || slot_stride < n)
+    return fail(TPR_ERR_SHAPE, "need n >= 0, nslots >= 0 and slot_stride >= n (got %lld, %d, %lld)", (long long)n,
+                nslots, (long long)slot_stride);
+  if (n == 0) return TPR_OK;
+  if (out == nullptr || (nslots > 0 && partials == nullptr))
+    return fail(TPR_ERR_NULLPTR, "out or partials is NULL");
+  if (nslots > 0) {
+    const uintptr_t o0 = reinterpret_cast<uintptr_t>(out), o1 = o0 + (uintptr_t)n * 4;
+    const uintptr_t p0 = reinterpret_cast<uintptr_t>(partials),
+                    p1 = p0 + ((uintptr_t)(nslots - 1) * (uintptr_t)slot_stride + (uintptr_t)n) * 4;
+    if (o0 < p1 && p0 < o1) return fail(TPR_ERR_VALUE, "out overlaps the partials");
+  }
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const hipError_t he = nslots == 0 ? tpr::launch_fill_zero(out, 1, n, n, s)
+                                    : tpr::launch_reduce_partials(partials, nslots, slot_stride, out, n, s);
+  if (he != hipSuccess) return hip_fail(he, "partial-sum reduction");
+  return TPR_OK;
+}
+
 // ---------------------------------------------------------------- TP MLP
 namespace {
 
-constexpr int kCUs = 256;    // compute units of an MI355X
 constexpr int kTile = 256;   // block tile of the bf16 GEMM
 
 // Rows of dH = gy W2^T computed in the fc1 launch of the plain bf16 MLP: T
@@ -251,7 +299,8 @@ int64_t cosched_rows(int dtype, int act, int tp, int64_t T, int64_t f) {
     nb += tn;
   }
   if (nb == 0) return 0;
-  const int64_t free = (kCUs - n1 % kCUs) % kCUs;
+  const int64_t cus = tpr::device_topology().cus;
+  const int64_t free = (cus - n1 % cus) % cus;
   return (free / nb) * kTile >= T ? T : 0;
 }
 

@@ -34,7 +34,16 @@ struct GemmBatch {
   GemmProb p[kMaxGroup];
   int count;
   int total_tiles;
+  int nxcd;  // XCDs of the device: workgroup i runs on XCD i mod nxcd (set by the launcher)
 };
+
+// Compute units and XCDs of the calling thread's current device, read from
+// the runtime once per device.  When no device answers (a workspace query on
+// a host without a GPU) the counts of a whole MI355X, (256, 8), stand in.
+struct Topology {
+  int cus, xcds;
+};
+Topology device_topology();
 
 enum Epilogue {
   EPI_F32 = 0,    // C (fp32) = acc

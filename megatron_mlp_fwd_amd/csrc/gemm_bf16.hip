@@ -214,6 +214,7 @@ bool aligned(const void* p, int bytes) { return (reinterpret_cast<uintptr_t>(p) 
 }  // namespace
 
 hipError_t launch_gemm_bf16(GemmBatch& b, bool a_kmajor, bool b_kmajor, int epi, hipStream_t s) {
+  b.nxcd = device_topology().xcds;
   int total = 0;
   bool vec = true, vec_c = true;
   for (int i = 0; i < b.count; ++i) {

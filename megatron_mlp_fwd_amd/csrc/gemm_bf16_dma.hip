@@ -354,11 +354,11 @@ __device__ __forceinline__ void gemm_tile(const GemmProb& P, int tm, int tn, uin
   }
 }
 
-// Block -> (problem, tile).  Every problem's tiles start at a multiple of 8
-// blocks (padding blocks exit), so a block's XCD (blockIdx % 8, the hardware's
-// round-robin) is its position within the problem modulo 8; each XCD gets one
-// contiguous run of the problem's tiles, walked in grouped raster order
-// (RASTER_M tile rows per group).
+// Block -> (problem, tile).  Every problem's tiles start at a multiple of X =
+// nxcd blocks (padding blocks exit), so a block's XCD (blockIdx % X, the
+// hardware's round-robin) is its position within the problem modulo X; each
+// XCD gets one contiguous run of the problem's tiles, walked in grouped
+// raster order (RASTER_M tile rows per group).
 // ALT_ACT: the instance for batches of activation epilogues other than GELU
 // (EPI_ACT problems only); the main instance keeps GELU as its one activation.
 template <bool ALT_ACT>
@@ -372,8 +372,9 @@ __global__ __launch_bounds__(NTH, 1) void gemm_bf16_dma_kernel(const GemmBatch b
   const GemmProb P = batch.p[g];  // a copy: keeps the by-value batch out of scratch
   const int ntiles = P.tiles_m * P.tiles_n;
   const int l = bid - P.tile_start;
-  const int per_xcd = (ntiles + 7) >> 3;
-  int local = (l & 7) * per_xcd + (l >> 3);
+  const int X = batch.nxcd;
+  const int per_xcd = (ntiles + X - 1) / X;
+  int local = (l % X) * per_xcd + l / X;
   if (local >= ntiles) return;
   const int per_group = RASTER_M * P.tiles_n;
   const int first_m = (local / per_group) * RASTER_M;
@@ -428,9 +429,11 @@ bool gemm_bf16_dma_eligible(const GemmProb& p, bool a_kmajor, bool b_kmajor, int
 }
 
 // Problems arrive with `kind` set; the launcher lays out the flattened grid
-// (each problem padded to a multiple of 8 blocks) and records whether each
-// problem's outputs allow vector stores (kind bit 8).
+// (each problem padded to a multiple of the device's XCD count) and records
+// whether each problem's outputs allow vector stores (kind bit 8).
 hipError_t launch_gemm_bf16_dma(GemmBatch& b, hipStream_t s) {
+  const int X = device_topology().xcds;
+  b.nxcd = X;
   int total = 0;
   for (int i = 0; i < b.count; ++i) {
     GemmProb& p = b.p[i];
@@ -438,7 +441,7 @@ hipError_t launch_gemm_bf16_dma(GemmBatch& b, hipStream_t s) {
     p.tiles_m = (p.M + BM - 1) / BM;
     p.tiles_n = (p.N + BN - 1) / BN;
     p.tile_start = total;
-    total += ((p.tiles_m * p.tiles_n + 7) / 8) * 8;
+    total += ((p.tiles_m * p.tiles_n + X - 1) / X) * X;
     const int cbytes = epi == EPI_F32 ? 16 : 8;
     const bool vec_c = aligned(p.C, cbytes) && p.ldc % 4 == 0 && (epi != EPI_ACT || aligned(p.aux_out, 8)) &&
                        (epi != EPI_MUL || aligned(p.aux_in, 8));

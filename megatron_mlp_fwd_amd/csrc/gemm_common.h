@@ -42,11 +42,11 @@ __device__ __forceinline__ uint32_t pack_bf16(float a, float b) {
 __device__ __forceinline__ float bf_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
 
-// Workgroups are handed to the 8 XCDs round-robin; renumber so that each XCD
+// Workgroups are handed to the X XCDs round-robin; renumber so that each XCD
 // walks a contiguous range of tiles (neighbouring tiles share its L2).
-__device__ __forceinline__ int xcd_remap(int bid, int total) {
-  const int per = total >> 3, rem = total & 7;
-  const int x = bid & 7, slot = bid >> 3;
+__device__ __forceinline__ int xcd_remap(int bid, int total, int X) {
+  const int per = total / X, rem = total % X;
+  const int x = bid % X, slot = bid / X;
   return x * per + (x < rem ? x : rem) + slot;
 }
 
@@ -55,7 +55,7 @@ struct TileCoord {
   int g, tm, tn;
 };
 __device__ __forceinline__ TileCoord locate_tile(const GemmBatch& batch) {
-  const int bid = xcd_remap((int)blockIdx.x, batch.total_tiles);
+  const int bid = xcd_remap((int)blockIdx.x, batch.total_tiles, batch.nxcd);
   int g = 0;
 #pragma unroll
   for (int i = 1; i < kMaxGroup; ++i)

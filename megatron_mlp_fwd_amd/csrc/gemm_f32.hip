@@ -90,6 +90,7 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(const GemmBatch batch, in
 }  // namespace
 
 hipError_t launch_gemm_f32(GemmBatch& b, bool a_kmajor, bool b_kmajor, int epi, hipStream_t s) {
+  b.nxcd = device_topology().xcds;
   int total = 0;
   for (int i = 0; i < b.count; ++i) {
     GemmProb& p = b.p[i];

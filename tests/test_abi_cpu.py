@@ -107,6 +107,20 @@ def test_mlp_and_ce_reject_bad_arguments(lib):
     assert h(2, 1, 4, 8, p, p, p, p, N, N, 0, N) == binding.TPR_ERR_WORKSPACE
 
 
+def test_partial_sum_rejects_bad_arguments(lib):
+    f = lib.tprank_partial_sum
+    p = ctypes.c_void_p(1 << 20)  # never dereferenced: validation stops first
+    assert f(2, -1, p, 8, p, N) == binding.TPR_ERR_SHAPE
+    assert f(-1, 8, p, 8, p, N) == binding.TPR_ERR_SHAPE
+    assert f(2, 8, p, 7, p, N) == binding.TPR_ERR_SHAPE              # slots overlap each other
+    assert f(2, 8, N, 8, p, N) == binding.TPR_ERR_NULLPTR
+    assert f(2, 8, p, 8, N, N) == binding.TPR_ERR_NULLPTR
+    out = ctypes.c_void_p((1 << 20) + 4 * 12)                       # inside the second slot
+    assert f(2, 8, p, 8, out, N) == binding.TPR_ERR_VALUE
+    assert b"overlaps" in lib.tprank_last_error()
+    assert f(2, 0, N, 0, N, N) == binding.TPR_OK                     # nothing to do, nothing enqueued
+
+
 def test_head_ce_workspace_and_bad_arguments(lib):
     ws = lib.vocab_parallel_head_ce_workspace_bytes
     # logits + dlogits (bf16), row losses, and 8 fp32 partials of dh

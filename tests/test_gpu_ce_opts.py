@@ -2,8 +2,9 @@
 positions, label smoothing) through the C ABI, against the fp64 oracle.
 
 Same tolerances as the plain cross-entropy: the loss within 1e-5 relative,
-dlogits within 1e-5 (fp32 logits) or 2e-2 (bf16 logits) of max |oracle|,
-padding columns and ignored rows exactly zero, maxima exact.
+dlogits within 1e-5 (fp32 logits) or 2e-2 (bf16 logits) of max |oracle| and
+element by element against the oracle's (p - q) / n (ce_checks.py), padding
+columns and ignored rows exactly zero, maxima exact.
 """
 import math
 import sys
@@ -13,6 +14,7 @@ import pytest
 import torch
 
 import workloads
+from ce_checks import assert_grad_elementwise, target_rows
 from oracle.ce_options import cross_entropy_opts, vocab_parallel_ce_opts
 
 pytestmark = pytest.mark.gpu
@@ -62,6 +64,9 @@ def check(tpr, logits, labels, parts, vv, ign, eps, stats=False):
     g = f64(dl)
     assert rel_err(g, wg) <= tol
     V = logits.shape[1]
+    counted = np.ones(len(y), dtype=bool) if ign is None else y != ign
+    q = target_rows(np.where(counted, y, 0), V, vv, eps, counted)
+    assert_grad_elementwise(g, wg, q, max(n, 1), "f32" if logits.dtype == torch.float32 else "bf16", "dlogits")
     assert not g[:, vv:].any()                              # padding columns
     if ign is not None:
         assert not g[y == ign].any()                        # ignored rows
@@ -144,24 +149,39 @@ def test_ce_opts_zero_rows(tpr):
     assert math.isnan(loss.item()) and dl.shape == (0, 16)
 
 
-def test_ce_opts_full_config_sampled(tpr):
+def test_ce_opts_full_config(tpr):
     # The measured case: 4096 x 128256 bf16 logits of a 128000-entry
-    # vocabulary, 8 shards, label smoothing 0.1, one position in eight ignored.
-    say("CE options 4096 x 128256 (128000 vocabulary), eps 0.1, 1/8 ignored")
+    # vocabulary, 8 shards, label smoothing 0.1, one position in eight
+    # ignored; every row against the oracle, in row blocks.
+    say("CE options 4096 x 128256 (128000 vocabulary), eps 0.1, 1/8 ignored, every row")
     T, V, vv, P, eps = 4096, 128256, 128000, 8, 0.1
     logits, labels = workloads.vocab_ce_opts(T, V, vv, seed=0, device=DEV)
+    out = (torch.empty((), device=DEV), torch.full((T, V), float("nan"), dtype=torch.bfloat16, device=DEV), None)
     loss, dl, _ = tpr.vocab_parallel_ce_opts_fwd_bwd(P, logits, labels, v_valid=vv, ignore_index=IGN,
-                                                     label_smoothing=eps)
+                                                     label_smoothing=eps, out=out)
     torch.cuda.synchronize()
     y = labels.cpu().numpy()
-    n = int((y != IGN).sum())
+    counted = y != IGN
+    n = int(counted.sum())
     rowsum = dl.float().sum(dim=1)
     assert rowsum.abs().max().item() <= 2.0 ** -7 / n
     assert not dl[:, vv:].any()
-    assert not dl[torch.as_tensor(y == IGN, device=DEV)].any()
+    assert not dl[torch.as_tensor(~counted, device=DEV)].any()
     z = logits.float().cpu().numpy()
-    rows = np.sort(np.random.default_rng(1).choice(T, 16, replace=False))
-    wl, _, wg, wn = cross_entropy_opts(z, y, vv, IGN, eps, grad_rows=rows)
-    assert wn == n
+    total = diff = scale = worst = 0.0
+    for lo in range(0, T, 256):
+        hi = min(T, lo + 256)
+        _, rl, g, nb = cross_entropy_opts(z[lo:hi], y[lo:hi], vv, IGN, eps)
+        total += rl.sum()
+        g *= nb / n                           # the block's mean -> the mean over all counted rows
+        got = f64(dl[lo:hi])
+        assert not np.isnan(got).any(), lo
+        diff = max(diff, float(np.abs(got - g).max()))
+        scale = max(scale, float(np.abs(g).max()))
+        c = counted[lo:hi]
+        q = target_rows(np.where(c, y[lo:hi], 0), V, vv, eps, c)
+        worst = max(worst, assert_grad_elementwise(got, g, q, n, "bf16", f"rows {lo}..{hi}"))
+    wl = total / n
     assert abs(loss.item() - wl) <= 1e-5 * abs(wl)
-    assert rel_err(f64(dl[rows]), wg) <= 2e-2
+    assert diff <= 2e-2 * scale
+    say("worst element / bound", round(worst, 3), "max-scaled error", diff / scale)

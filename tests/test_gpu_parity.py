@@ -2,10 +2,13 @@
 
 Tolerances (max |gpu - oracle| over an output tensor, relative to max |oracle|):
 1e-5 for fp32 inputs and 2e-2 for bf16 inputs; shard ranges and shapes are
-bit-exact.  The oracle sees exactly the values the GPU sees (bf16 widened to
-fp64) and rounds no intermediate.  Full-size workloads are checked on sampled
-outputs that the oracle computes one by one, plus properties that hold at any
-size.
+bit-exact.  Cross-entropy gradients are also checked element by element
+(ce_checks.py: every softmax term against a bound derived from the kernels'
+roundings), since at a large vocabulary the max-scaled bound cannot see the
+softmax part.  The oracle sees exactly the values the GPU sees (bf16 widened
+to fp64) and rounds no intermediate.  Full-size workloads are compared on
+every output element (outputs pre-filled with NaN, so a tile never written
+fails), the oracle working through them in row blocks.
 """
 import sys
 
@@ -17,6 +20,7 @@ import torch
 
 import oracle
 import workloads
+from ce_checks import assert_grad_elementwise, target_rows
 
 pytestmark = pytest.mark.gpu
 
@@ -46,6 +50,10 @@ def rel_err(got, want):
 
 def tol_of(dtype):
     return TOL_F32 if dtype == torch.float32 else TOL_BF16
+
+
+def out_kind(dtype):
+    return "f32" if dtype == torch.float32 else "bf16"
 
 
 @pytest.fixture(scope="module")
@@ -155,25 +163,34 @@ def test_bf16_gemm_more_parts_than_rows(tpr):
                 assert rel_err(f64(o), w) <= 1e-4
 
 
-def test_inner_gemm_70b_rank_sampled(tpr):
-    # One TP=8 rank's inner-axis shard of the 70B MLP: M=8192, K_r=1024, N=8192.
-    say("inner GEMM 8192x1024x8192 bf16, sampled")
+def _nan_out(*shapes):
+    return tuple(torch.full(sh, float("nan"), device=DEV) for sh in shapes)
+
+
+def test_inner_gemm_70b_rank_full(tpr):
+    # One TP=8 rank's inner-axis shard of the 70B MLP: M=8192, K_r=1024,
+    # N=8192, every element of Y, dA and dB at 1 and 8 parts.  bf16 inputs are
+    # exact in the oracle and products accumulate in fp32, so beside the 2e-2
+    # contract the results sit within 1e-4 of max |oracle|.
+    say("inner GEMM 8192x1024x8192 bf16, every element, parts 1 and 8")
     M, K, N = 8192, 1024, 8192
     a, b, g = workloads.inner_gemm(M, K, N, seed=5, device=DEV)
-    Y, dA, dB = tpr.sharded_matmul_fwd_bwd("inner", 1, a, b, g)
-    torch.cuda.synchronize()
-    rng = np.random.default_rng(1)
-    rows = np.sort(rng.choice(M, 12, replace=False))
-    cols = np.sort(rng.choice(N, 12, replace=False))
-    A, B, G = f64(a), f64(b), f64(g)
-    assert rel_err(f64(Y[rows]), A[rows] @ B) <= TOL_BF16
-    assert rel_err(f64(dA[rows]), G[rows] @ B.T) <= TOL_BF16
-    assert rel_err(f64(dB[:, cols]), A.T @ G[:, cols]) <= TOL_BF16
-    # the same rank split 8 ways again must agree with itself
-    Y8, dA8, dB8 = tpr.sharded_matmul_fwd_bwd("inner", 8, a, b, g)
-    torch.cuda.synchronize()
-    assert rel_err(f64(Y8[rows]), A[rows] @ B) <= TOL_BF16
-    assert torch.equal(dA8, dA) and torch.equal(dB8, dB)
+    want = oracle.matmul_grads(f64(a), f64(b), f64(g))
+    first = None
+    for parts in (1, 8):
+        got = tpr.sharded_matmul_fwd_bwd("inner", parts, a, b, g, out=_nan_out((M, N), (M, K), (K, N)))
+        torch.cuda.synchronize()
+        for name, w, o in zip(("Y", "dA", "dB"), want, got):
+            e = rel_err(f64(o), w)
+            say("parts", parts, name, "rel err", e)
+            assert e <= 1e-4, (parts, name, e)
+        if first is None:
+            first = got
+        else:  # stacked outputs do not depend on the split; Y only through its sum
+            assert torch.equal(got[1], first[1]) and torch.equal(got[2], first[2])
+        del got
+    del first
+    torch.cuda.empty_cache()
 
 
 @pytest.mark.parametrize("K", [32736, 32768])
@@ -198,6 +215,60 @@ def test_bf16_gemm_operand_size_limit(tpr, K):
     assert rel_err(f64(dB[ki]), f64(a[:, ki]).T @ G) <= 1e-4
     del Y, dA, dB, a, b, g
     torch.cuda.empty_cache()
+
+
+# ---------------------------------------------------------------- partial sum
+
+def _slot_order_sum(p):
+    # the definition evaluated in the library's order: fp32 adds, slot by slot
+    acc = p[0].copy()
+    for r in range(1, p.shape[0]):
+        acc = (acc + p[r]).astype(np.float32)
+    return acc
+
+
+@pytest.mark.parametrize("nslots,n", [(1, 1000), (2, 4096), (3, 4099), (8, 1 << 20), (9, 5000), (17, 4096),
+                                      (8, 8192 * 8192)])
+def test_partial_sum(tpr, nslots, n):
+    # Cross-rank partial sum through tprank_partial_sum: the same bits as
+    # fp32 adds in slot order, within fp32 rounding of the fp64 sum.
+    say("partial sum", nslots, n)
+    g = torch.Generator(device=DEV)
+    g.manual_seed(nslots * 7 + n % 1000)
+    parts = torch.randn(nslots, n, generator=g, device=DEV)
+    out = torch.full((n,), float("nan"), device=DEV)
+    got = tpr.partial_sum(parts, out=out)
+    torch.cuda.synchronize()
+    p = parts.cpu().numpy()
+    np.testing.assert_array_equal(got.cpu().numpy(), _slot_order_sum(p))
+    want = p.astype(np.float64).sum(axis=0)
+    assert np.abs(got.cpu().numpy() - want).max() <= nslots * 2.0 ** -23 * np.abs(p).sum(axis=0).max()
+    del parts, out, got
+    torch.cuda.empty_cache()
+
+
+def test_partial_sum_strided_and_edges(tpr):
+    import ctypes
+    lib = tpr.load_library()
+    stream = torch.cuda.current_stream().cuda_stream
+    nslots, n, stride = 5, 1000, 1024      # slots 1024 floats apart, 1000 used
+    g = torch.Generator(device=DEV)
+    g.manual_seed(3)
+    buf = torch.randn(nslots, stride, generator=g, device=DEV)
+    out = torch.full((n + 8,), float("nan"), device=DEV)
+    assert lib.tprank_partial_sum(nslots, n, buf.data_ptr(), stride, out.data_ptr(), stream) == 0
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(out[:n].cpu().numpy(), _slot_order_sum(buf[:, :n].cpu().numpy()))
+    assert torch.isnan(out[n:]).all()      # nothing past the n outputs
+    # no slots: the empty sum is zero
+    assert lib.tprank_partial_sum(0, n, None, n, out.data_ptr(), stream) == 0
+    torch.cuda.synchronize()
+    assert not out[:n].any() and torch.isnan(out[n:]).all()
+    # rejected before any launch
+    assert lib.tprank_partial_sum(2, 10, buf.data_ptr(), 5, out.data_ptr(), stream) == tpr.binding.TPR_ERR_SHAPE
+    assert lib.tprank_partial_sum(2, 10, buf.data_ptr(), 16, buf.data_ptr() + 8, stream) == \
+        tpr.binding.TPR_ERR_VALUE
+    assert lib.tprank_partial_sum(2, 10, None, 16, out.data_ptr(), stream) == tpr.binding.TPR_ERR_NULLPTR
 
 
 # ---------------------------------------------------------------- TP MLP
@@ -263,32 +334,33 @@ def test_mlp_zero_sizes(tpr):
                 np.testing.assert_array_equal(f64(o), w)
 
 
-def _mlp_rank_sampled(tpr, T, d, f, seed):
+def _mlp_rank_full(tpr, T, d, f, seed):
+    # Every element of y, dx, dw1 and dw2 against the fp64 oracle; the
+    # outputs start as NaN so that a tile the launches never write fails.
     x, w1, w2, gy = workloads.rank_mlp(T, d, f, seed=seed, device=DEV)
-    y, dx, dw1, dw2 = tpr.tp_mlp_fwd_bwd(1, x, w1, w2, gy, "math")
+    out = _nan_out((T, d), (T, d), (d, f), (f, d))
+    got = tpr.tp_mlp_fwd_bwd(1, x, w1, w2, gy, "math", out=out)
     torch.cuda.synchronize()
-    rng = np.random.default_rng(seed)
-    rows = np.sort(rng.choice(T, 8, replace=False))
-    cols = np.sort(rng.choice(f, 8, replace=False))
-    s = oracle.mlp_sampled(f64(x), f64(w1), f64(w2), f64(gy), rows, cols, "math")
-    errs = dict(y=rel_err(f64(y[rows]), s["y"]), dx=rel_err(f64(dx[rows]), s["dx"]),
-                dw1=rel_err(f64(dw1[:, cols]), s["dw1_cols"]), dw2=rel_err(f64(dw2[cols]), s["dw2_rows"]))
-    say("sampled rel errs", errs)
+    want = oracle.mlp_fwd_bwd(f64(x), f64(w1), f64(w2), f64(gy), "math")
+    errs = {}
+    for name, w, o in zip(("y", "dx", "dw1", "dw2"), want, got):
+        h = f64(o)
+        assert not np.isnan(h).any(), name
+        errs[name] = rel_err(h, w)
+    say("rel errs", errs)
     for k, e in errs.items():
         assert e <= TOL_BF16, (k, e)
-    # properties at full size: finite everywhere
-    for t in (y, dx, dw1, dw2):
-        assert torch.isfinite(t).all()
 
 
-def test_mlp_llama3_8b_tp8_rank_sampled(tpr):
-    say("Llama-3-8B TP=8 rank MLP T=4096 d=4096 f=1792, sampled")
-    _mlp_rank_sampled(tpr, 4096, 4096, 1792, seed=8)
+def test_mlp_llama3_8b_tp8_rank_full(tpr):
+    say("Llama-3-8B TP=8 rank MLP T=4096 d=4096 f=1792, every element")
+    _mlp_rank_full(tpr, 4096, 4096, 1792, seed=8)
 
 
-def test_mlp_llama3_70b_tp8_rank_sampled(tpr):
-    say("Llama-3-70B TP=8 rank MLP T=8192 d=8192 f=3584, sampled")
-    _mlp_rank_sampled(tpr, 8192, 8192, 3584, seed=70)
+def test_mlp_llama3_70b_tp8_rank_full(tpr):
+    say("Llama-3-70B TP=8 rank MLP T=8192 d=8192 f=3584, every element")
+    _mlp_rank_full(tpr, 8192, 8192, 3584, seed=70)
+    torch.cuda.empty_cache()
 
 
 # ---------------------------------------------------------------- vocab CE
@@ -308,6 +380,7 @@ def test_ce_small(tpr, V, parts, dtype, stats):
     tol = tol_of(dtype)
     assert abs(loss.item() - wl) <= tol * abs(wl)
     assert rel_err(f64(dl), wg) <= tol
+    assert_grad_elementwise(f64(dl), wg, target_rows(y, V), T, out_kind(dtype), "dlogits")
     if not stats:
         assert st is None
         return
@@ -333,6 +406,8 @@ def test_ce_bf16_row_split_edges(tpr, V):
     wl, _, wg = oracle.cross_entropy(z, y, grad_rows=np.arange(T))
     assert abs(loss.item() - wl) <= 1e-5 * abs(wl)
     assert rel_err(f64(dl), wg) <= TOL_BF16
+    # every element, the LDS-resident part of the row included
+    assert_grad_elementwise(f64(dl), wg, target_rows(y, V), T, "bf16", "dlogits")
 
 
 # Per-shard statistics in the paired kernel: equal shards of >= 64 vectors of
@@ -355,6 +430,9 @@ def test_ce_bf16_shard_stats_paired(tpr, vps, parts, monkeypatch):
     wl, _, wg, wst = oracle.vocab_parallel_ce(z, y, parts)
     assert abs(loss.item() - wl) <= 1e-5 * abs(wl)
     assert rel_err(f64(dl), wg) <= TOL_BF16
+    q = target_rows(y, V)
+    assert_grad_elementwise(f64(dl), wg, q, T, "bf16", "dlogits (paired kernel)")
+    assert_grad_elementwise(f64(dl1), wg, q, T, "bf16", "dlogits (one-row kernel)")
     gst = f64(st)
     np.testing.assert_array_equal(gst[:, :, 0], wst[:, :, 0])           # maxima are exact
     np.testing.assert_allclose(gst[:, :, 1], wst[:, :, 1], rtol=1e-5, atol=1e-30)
@@ -373,12 +451,39 @@ def test_ce_zero_rows(tpr):
     assert loss.item() == 0.0 and dl.shape == (0, 16)
 
 
+def _ce_check_all_rows(dl, z, y, loss, what, block=256):
+    """Every row of a full-size CE result against the oracle, in row blocks:
+    the loss within 1e-5, dlogits within 2e-2 max |oracle| over the whole
+    tensor and element by element (ce_checks.py)."""
+    T, V = z.shape
+    row_loss = np.empty(T)
+    diff = scale = worst = 0.0
+    for lo in range(0, T, block):
+        hi = min(T, lo + block)
+        _, rl, g = oracle.cross_entropy(z[lo:hi], y[lo:hi])
+        row_loss[lo:hi] = rl
+        g *= (hi - lo) / T            # the block's mean -> the mean over all T rows
+        got = f64(dl[lo:hi])
+        assert not np.isnan(got).any(), (what, lo)
+        diff = max(diff, float(np.abs(got - g).max()))
+        scale = max(scale, float(np.abs(g).max()))
+        worst = max(worst, assert_grad_elementwise(got, g, target_rows(y[lo:hi], V), T, "bf16",
+                                                   f"{what}, rows {lo}..{hi}"))
+    wl = row_loss.mean()
+    assert abs(loss.item() - wl) <= 1e-5 * abs(wl), (loss.item(), wl)
+    assert diff <= TOL_BF16 * scale, (diff, scale)
+    say(what, "worst element / bound", round(worst, 3), "max-scaled error", diff / scale)
+    return row_loss
+
+
 def test_ce_full_config(tpr):
     # 4096 positions x vocab 128256, 8 contiguous shards of 16032, bf16 ~ N(0, 2).
-    say("vocab CE 4096 x 128256 bf16, 8 shards")
+    say("vocab CE 4096 x 128256 bf16, 8 shards, every row")
     T, V, P = 4096, 128256, 8
     logits, labels = workloads.vocab_ce(T=T, V=V, seed=0, device=DEV)
-    loss, dl, st = tpr.vocab_parallel_ce_fwd_bwd(P, logits, labels, shard_stats=True)
+    out = (torch.empty((), device=DEV), torch.full((T, V), float("nan"), dtype=torch.bfloat16, device=DEV),
+           torch.full((T, P, 3), float("nan"), device=DEV))
+    loss, dl, st = tpr.vocab_parallel_ce_fwd_bwd(P, logits, labels, shard_stats=True, out=out)
     torch.cuda.synchronize()
     # every row's gradient sums to 0 (softmax minus one-hot); rounding each term
     # to bf16 (unit roundoff 2^-8) over sum_j |g_j| = 2 (1 - p_y) / T bounds the
@@ -387,33 +492,34 @@ def test_ce_full_config(tpr):
     assert rowsum.abs().max().item() <= 2.0 ** -7 / T
     z = logits.float().cpu().numpy()
     y = labels.cpu().numpy()
-    rows = np.sort(np.random.default_rng(0).choice(T, 16, replace=False))
-    wl, _, wg = oracle.cross_entropy(z, y, grad_rows=rows)
-    assert abs(loss.item() - wl) <= 1e-5 * abs(wl)
-    assert rel_err(f64(dl[rows]), wg) <= TOL_BF16
-    _, _, _, wst = oracle.vocab_parallel_ce(z[rows], y[rows], P)
-    gst = f64(st[rows])
-    np.testing.assert_array_equal(gst[:, :, 0], wst[:, :, 0])
-    np.testing.assert_allclose(gst[:, :, 1], wst[:, :, 1], rtol=1e-5)
-    np.testing.assert_allclose(gst[:, :, 2], wst[:, :, 2], rtol=1e-6, atol=1e-6)
+    rl = _ce_check_all_rows(dl, z, y, loss, "CE with shard stats")
+    _, _, _, wst = oracle.vocab_parallel_ce(z[:64], y[:64], P)
+    gst = f64(st)
+    assert not np.isnan(gst).any()
+    np.testing.assert_array_equal(gst[:64, :, 0], wst[:, :, 0])
+    np.testing.assert_allclose(gst[:64, :, 1], wst[:, :, 1], rtol=1e-5)
+    np.testing.assert_allclose(gst[:64, :, 2], wst[:, :, 2], rtol=1e-6, atol=1e-6)
+    # the rest of the rows: the statistics combine to the row's loss and max
+    m = gst[:, :, 0].max(axis=1)
+    np.testing.assert_array_equal(m, z.max(axis=1))
+    lse = np.log(gst[:, :, 1].sum(axis=1)) + m
+    zy = z[np.arange(T), y]
+    np.testing.assert_allclose(gst[:, :, 2].sum(axis=1), zy - m, rtol=1e-6, atol=1e-6)
+    np.testing.assert_allclose(lse - zy, rl, rtol=2e-6, atol=1e-6)
 
 
 def test_ce_full_config_no_stats(tpr):
     # The benchmarked call: 4096 x 128256, 8 shards, no per-shard statistics.
-    say("vocab CE 4096 x 128256 bf16, 8 shards, no stats")
+    say("vocab CE 4096 x 128256 bf16, 8 shards, no stats, every row")
     T, V, P = 4096, 128256, 8
     logits, labels = workloads.vocab_ce(T=T, V=V, seed=0, device=DEV)
-    loss, dl, st = tpr.vocab_parallel_ce_fwd_bwd(P, logits, labels)
+    out = (torch.empty((), device=DEV), torch.full((T, V), float("nan"), dtype=torch.bfloat16, device=DEV), None)
+    loss, dl, st = tpr.vocab_parallel_ce_fwd_bwd(P, logits, labels, out=out)
     torch.cuda.synchronize()
     assert st is None
     rowsum = dl.float().sum(dim=1)
     assert rowsum.abs().max().item() <= 2.0 ** -7 / T
-    z = logits.float().cpu().numpy()
-    y = labels.cpu().numpy()
-    rows = np.sort(np.random.default_rng(1).choice(T, 16, replace=False))
-    wl, _, wg = oracle.cross_entropy(z, y, grad_rows=rows)
-    assert abs(loss.item() - wl) <= 1e-5 * abs(wl)
-    assert rel_err(f64(dl[rows]), wg) <= TOL_BF16
+    _ce_check_all_rows(dl, logits.float().cpu().numpy(), labels.cpu().numpy(), loss, "CE without shard stats")
 
 
 def test_determinism(tpr):
@@ -435,6 +541,56 @@ def test_determinism(tpr):
 
 # ---------------------------------------------------------------- vocab head + CE
 
+U24 = 2.0 ** -24
+
+
+def _head_stages(tpr, h, w, y, parts, layout):
+    """Run the head and return (loss, dh, dw, logits, dlogits): the last two
+    read from the workspace, where the entry point leaves them (logits at
+    byte 0, dlogits at the next 256-byte boundary)."""
+    T, d = h.shape
+    V = w.shape[1] if layout == "math" else w.shape[0]
+    nb = tpr.vocab_parallel_head_ce_workspace_bytes(parts, h.dtype, T, d, V)
+    ws = torch.full((nb,), 0xFF, dtype=torch.uint8, device=DEV)  # NaN in bf16 and fp32
+    loss, dh, dw = tpr.vocab_parallel_head_ce_fwd_bwd(parts, h, w, y, w_layout=layout, workspace=ws)
+    torch.cuda.synchronize()
+    tv = T * V * h.element_size()
+    off = (tv + 255) // 256 * 256
+    logits = ws[:tv].view(h.dtype).view(T, V)
+    dl = ws[off:off + tv].view(h.dtype).view(T, V)
+    return loss, dh, dw, logits, dl
+
+
+def _check_head_stages(h, w, y, layout, parts, loss, dh, dw, logits, dl, dtype):
+    """Each stage against the oracle on that stage's exact inputs, element
+    by element: logits = h W (rounded once to the compute dtype, fp32
+    accumulation over d: |err| <= u |z| + d 2^-24 (|h| |W|)); dlogits =
+    the CE gradient of the GPU's own logits (ce_checks.py); dh = dlogits W^T
+    and dW = h^T dlogits of the GPU's own dlogits (fp32 accumulation over V,
+    plus the rank-order sum of the parts: (V + parts) 2^-24 (|dl| |W|^T))."""
+    H, Wm = f64(h), f64(w if layout == "math" else w.t())
+    T, d = H.shape
+    V = Wm.shape[1]
+    u = U24 if dtype == torch.float32 else 2.0 ** -8
+    z_ref = H @ Wm
+    z = f64(logits)
+    assert not np.isnan(z).any()
+    bound = u * np.abs(z_ref) + d * U24 * (np.abs(H) @ np.abs(Wm))
+    assert (np.abs(z - z_ref) <= bound).all(), float((np.abs(z - z_ref) / bound).max())
+    yy = y.cpu().numpy()
+    wl, _, g_ref = oracle.cross_entropy(z, yy)
+    assert abs(loss.item() - wl) <= 1e-5 * abs(wl) + 1e-7
+    G = f64(dl)
+    assert_grad_elementwise(G, g_ref, target_rows(yy, V), T, out_kind(dtype), "head dlogits")
+    dh_ref = G @ Wm.T
+    bh = (V + parts) * U24 * (np.abs(G) @ np.abs(Wm.T))
+    assert (np.abs(f64(dh) - dh_ref) <= bh).all(), float((np.abs(f64(dh) - dh_ref) / bh).max())
+    dw_ref = H.T @ G
+    bw = (T + 1) * U24 * (np.abs(H.T) @ np.abs(G))
+    got_dw = f64(dw if layout == "math" else dw.t())
+    assert (np.abs(got_dw - dw_ref) <= bw).all(), float((np.abs(got_dw - dw_ref) / bw).max())
+
+
 @pytest.mark.parametrize("layout", ["math", "torch"])
 @pytest.mark.parametrize("parts", [1, 3, 8])
 @pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
@@ -445,13 +601,13 @@ def test_head_ce(tpr, T, d, V, dtype, parts, layout):
     # the probabilities carry a relative error of about |z| 2^-9.
     h, w, y = workloads.vocab_head(T, d, V, seed=T + d + V + parts, device=DEV, dtype=dtype,
                                    w_std=2.0 / math.sqrt(d), w_layout=layout)
-    loss, dh, dw = tpr.vocab_parallel_head_ce_fwd_bwd(parts, h, w, y, w_layout=layout)
-    torch.cuda.synchronize()
+    loss, dh, dw, logits, dl = _head_stages(tpr, h, w, y, parts, layout)
     wl, wdh, wdw = oracle.head_ce(f64(h), f64(w), y.cpu().numpy(), layout)
     tol = tol_of(dtype)
     assert abs(loss.item() - wl) <= tol * abs(wl)
     assert rel_err(f64(dh), wdh) <= tol
     assert rel_err(f64(dw), wdw) <= tol
+    _check_head_stages(h, w, y, layout, parts, loss, dh, dw, logits, dl, dtype)
 
 
 def test_head_ce_zero_rows(tpr):
@@ -465,16 +621,16 @@ def test_head_ce_zero_rows(tpr):
     assert torch.count_nonzero(dw).item() == 0
 
 
-def test_head_ce_llama3_8b_sized_sampled(tpr):
+def test_head_ce_llama3_8b_sized(tpr):
     # Llama-3-8B hidden size with a 32000-entry vocabulary, 8 shards (the
     # full 128256 vocabulary is the benchmark's; the fp64 oracle of a smaller
-    # vocabulary keeps the test in seconds), bf16.
+    # vocabulary keeps the test in seconds), bf16, every element of every stage.
     say("vocab head + CE T=512 d=4096 V=32000 bf16, 8 shards")
     T, d, V = 512, 4096, 32000
     h, w, y = workloads.vocab_head(T, d, V, seed=3, device=DEV, w_std=2.0 / math.sqrt(d))
-    loss, dh, dw = tpr.vocab_parallel_head_ce_fwd_bwd(8, h, w, y)
-    torch.cuda.synchronize()
+    loss, dh, dw, logits, dl = _head_stages(tpr, h, w, y, 8, "math")
     wl, wdh, wdw = oracle.head_ce(f64(h), f64(w), y.cpu().numpy())
     assert abs(loss.item() - wl) <= TOL_BF16 * abs(wl)
     assert rel_err(f64(dh), wdh) <= TOL_BF16
     assert rel_err(f64(dw), wdw) <= TOL_BF16
+    _check_head_stages(h, w, y, "math", 8, loss, dh, dw, logits, dl, torch.bfloat16)
