@@ -292,6 +292,22 @@ int vocab_parallel_ce_fwd_bwd(int parts, int dtype, int64_t T, int64_t V,
                               float* loss, void* dlogits, float* shard_stats,
                               void* ws, size_t ws_bytes, void* stream);
 
+/*
+ * The same call for callers that cannot allocate device memory: code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc.
+ * It takes no workspace: the per-row losses live in a static array inside
+ * the library, 2^18 fp32 (1 MiB) per device, held until the process ends;
+ * the call itself allocates nothing (its first call on a device only looks
+ * up that array's address there).  Arguments, results and errors are those of
+ * vocab_parallel_ce_fwd_bwd(), plus WORKSPACE when T > 2^18 (the array's
+ * capacity).  Every call on one device shares that device's array, so calls
+ * that overlap in time on one device (different streams, no ordering between
+ * them) race and give undefined results; calls ordered on one stream do not.
+ */
+int vocab_parallel_ce_fwd_bwd_noalloc(int parts, int dtype, int64_t T, int64_t V,
+                                      const void* logits, const int64_t* labels,
+                                      float* loss, void* dlogits, float* shard_stats, void* stream);
+
 /* ---- cross-entropy options: padded vocabulary, ignore index, smoothing - */
 /*
  * Bytes of workspace vocab_parallel_ce_opts_fwd_bwd() needs (the T per-row

@@ -13,7 +13,7 @@ from .binding import (ACTS, AXES, DTYPES, LIB_PATH, W_LAYOUTS, TprError, load_li
                       sharded_matmul_fwd_bwd, sharded_matmul_workspace_bytes, tp_mlp_fwd_bwd,
                       tp_mlp_workspace_bytes, tp_mlp_act_fwd_bwd, tp_mlp_act_workspace_bytes,
                       tp_attn_proj_fwd_bwd, tp_attn_proj_workspace_bytes,
-                      vocab_parallel_ce_fwd_bwd, vocab_parallel_ce_workspace_bytes,
+                      vocab_parallel_ce_fwd_bwd, vocab_parallel_ce_workspace_bytes, vocab_parallel_ce_fwd_bwd_noalloc,
                       vocab_parallel_ce_opts_fwd_bwd, vocab_parallel_ce_opts_workspace_bytes,
                       vocab_parallel_head_ce_fwd_bwd, vocab_parallel_head_ce_workspace_bytes)
 
@@ -22,7 +22,7 @@ __all__ = [
     "sharded_matmul_fwd_bwd", "sharded_matmul_workspace_bytes", "tp_mlp_fwd_bwd", "tp_mlp_workspace_bytes",
     "tp_mlp_act_fwd_bwd", "tp_mlp_act_workspace_bytes",
     "tp_attn_proj_fwd_bwd", "tp_attn_proj_workspace_bytes",
-    "vocab_parallel_ce_fwd_bwd", "vocab_parallel_ce_workspace_bytes",
+    "vocab_parallel_ce_fwd_bwd", "vocab_parallel_ce_workspace_bytes", "vocab_parallel_ce_fwd_bwd_noalloc",
     "vocab_parallel_ce_opts_fwd_bwd", "vocab_parallel_ce_opts_workspace_bytes",
     "vocab_parallel_head_ce_fwd_bwd", "vocab_parallel_head_ce_workspace_bytes",
 ]

@@ -39,6 +39,7 @@ _SIGS = {
     "tp_attn_proj_fwd_bwd": (_i32, [_i32, _i32, _i32, _i64, _i64, _i32, _i32, _i32] + [_vp] * 13 + [_sz, _vp]),
     "vocab_parallel_ce_workspace_bytes": (_sz, [_i32, _i64, _i64]),
     "vocab_parallel_ce_fwd_bwd": (_i32, [_i32, _i32, _i64, _i64, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
+    "vocab_parallel_ce_fwd_bwd_noalloc": (_i32, [_i32, _i32, _i64, _i64, _vp, _vp, _vp, _vp, _vp, _vp]),
     "vocab_parallel_ce_opts_workspace_bytes": (_sz, [_i32, _i64, _i64]),
     "vocab_parallel_ce_opts_fwd_bwd": (_i32, [_i32, _i32, _i64, _i64, _i64, _i64, ctypes.c_float, _vp, _vp, _vp, _vp,
                                               _vp, _vp, _sz, _vp]),
@@ -379,6 +380,31 @@ def vocab_parallel_ce_fwd_bwd(parts, logits, labels, shard_stats=False, out=None
         ws, wsb = _workspace(lib.vocab_parallel_ce_workspace_bytes(parts, T, V), dev, workspace)
         _check(lib.vocab_parallel_ce_fwd_bwd(parts, DTYPES[dt], T, V, _ptr(logits), _ptr(labels), loss.data_ptr(),
                                              _ptr(dlogits), _ptr(stats), _ptr(ws), wsb, on.handle))
+    return loss, dlogits, stats
+
+
+def vocab_parallel_ce_fwd_bwd_noalloc(parts, logits, labels, out, stream=None):
+    """vocab_parallel_ce_fwd_bwd for callers that cannot allocate: ``out`` =
+    (loss, dlogits, stats or None) must be supplied, and the library keeps the
+    per-row losses in its own static device array (T <= 2^18)."""
+    lib = load_library()
+    dt = logits.dtype
+    if dt not in DTYPES:
+        raise ValueError(f"unsupported dtype {dt}")
+    if logits.dim() != 2:
+        raise ValueError("logits must be 2-D")
+    T, V = logits.shape
+    dev = logits.device
+    _need(logits, "logits", (T, V), dt, dev)
+    _need(labels, "labels", (T,), torch.int64, dev)
+    loss, dlogits, stats = out
+    _need(loss, "loss", (), torch.float32, dev)
+    _need(dlogits, "dlogits", (T, V), dt, dev)
+    if stats is not None:
+        _need(stats, "shard_stats", (T, parts, 3), torch.float32, dev)
+    with _On(dev, stream) as on:
+        _check(lib.vocab_parallel_ce_fwd_bwd_noalloc(parts, DTYPES[dt], T, V, _ptr(logits), _ptr(labels),
+                                                     loss.data_ptr(), _ptr(dlogits), _ptr(stats), on.handle))
     return loss, dlogits, stats
 
 

@@ -626,9 +626,13 @@ size_t vocab_parallel_ce_workspace_bytes(int parts, int64_t T, int64_t V) {
   return align256((size_t)T * 4);
 }
 
-int vocab_parallel_ce_fwd_bwd(int parts, int dtype, int64_t T, int64_t V, const void* logits, const int64_t* labels,
-                              float* loss, void* dlogits, float* shard_stats, void* ws, size_t ws_bytes,
-                              void* stream) {
+}  // extern "C"
+
+namespace {
+
+// Checks shared by the two plain CE entry points (everything but the workspace).
+int ce_args_checked(int parts, int dtype, int64_t T, int64_t V, const void* logits, const int64_t* labels,
+                    const float* loss, const void* dlogits) {
   if (T < 0 || V < 0 || T > UINT_MAX || V / 8 > INT_MAX)
     return fail(TPR_ERR_SHAPE, "T and V out of range (got %lld, %lld)", (long long)T, (long long)V);
   if (T > 0 && V == 0) return fail(TPR_ERR_SHAPE, "V must be >= 1 when T > 0");
@@ -636,15 +640,17 @@ int vocab_parallel_ce_fwd_bwd(int parts, int dtype, int64_t T, int64_t V, const 
   if (!dtype_ok(dtype)) return fail(TPR_ERR_DTYPE, "unknown dtype %d", dtype);
   if (loss == nullptr || (T > 0 && (logits == nullptr || labels == nullptr || dlogits == nullptr)))
     return fail(TPR_ERR_NULLPTR, "loss, logits, labels or dlogits is NULL");
-  const size_t need = vocab_parallel_ce_workspace_bytes(parts, T, V);
-  if (ws_bytes < need || (need > 0 && ws == nullptr))
-    return fail(TPR_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", need, ws_bytes);
+  return TPR_OK;
+}
+
+int ce_launch(int parts, int dtype, int64_t T, int64_t V, const void* logits, const int64_t* labels, float* loss,
+              void* dlogits, float* shard_stats, float* row_loss, void* stream) {
   tpr::CeArgs a{};
   a.logits = logits;
   a.labels = labels;
   a.dlogits = dlogits;
   a.shard_stats = shard_stats;
-  a.row_loss = static_cast<float*>(ws);
+  a.row_loss = row_loss;
   a.loss = loss;
   a.T = T;
   a.V = V;
@@ -653,6 +659,35 @@ int vocab_parallel_ce_fwd_bwd(int parts, int dtype, int64_t T, int64_t V, const 
   const hipError_t he = tpr::launch_vocab_ce(a, static_cast<hipStream_t>(stream));
   if (he != hipSuccess) return hip_fail(he, "vocab CE launch");
   return TPR_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int vocab_parallel_ce_fwd_bwd(int parts, int dtype, int64_t T, int64_t V, const void* logits, const int64_t* labels,
+                              float* loss, void* dlogits, float* shard_stats, void* ws, size_t ws_bytes,
+                              void* stream) {
+  const int st = ce_args_checked(parts, dtype, T, V, logits, labels, loss, dlogits);
+  if (st != TPR_OK) return st;
+  const size_t need = vocab_parallel_ce_workspace_bytes(parts, T, V);
+  if (ws_bytes < need || (need > 0 && ws == nullptr))
+    return fail(TPR_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", need, ws_bytes);
+  return ce_launch(parts, dtype, T, V, logits, labels, loss, dlogits, shard_stats, static_cast<float*>(ws), stream);
+}
+
+int vocab_parallel_ce_fwd_bwd_noalloc(int parts, int dtype, int64_t T, int64_t V, const void* logits,
+                                      const int64_t* labels, float* loss, void* dlogits, float* shard_stats,
+                                      void* stream) {
+  const int st = ce_args_checked(parts, dtype, T, V, logits, labels, loss, dlogits);
+  if (st != TPR_OK) return st;
+  if (T > tpr::kCeStaticRows)
+    return fail(TPR_ERR_WORKSPACE, "T = %lld rows exceed the %lld rows of the library's static scratch", (long long)T,
+                (long long)tpr::kCeStaticRows);
+  float* rows = nullptr;
+  const hipError_t he = tpr::ce_static_scratch(&rows);
+  if (he != hipSuccess) return hip_fail(he, "static scratch of the current device");
+  return ce_launch(parts, dtype, T, V, logits, labels, loss, dlogits, shard_stats, rows, stream);
 }
 
 // ---------------------------------------------------------------- CE options

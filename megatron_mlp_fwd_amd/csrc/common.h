@@ -117,4 +117,10 @@ struct CeArgs {
 };
 hipError_t launch_vocab_ce(const CeArgs& a, hipStream_t s);
 
+// Rows of the CE's static per-row-loss array (1 MiB of fp32 per device), and
+// its device address on the current device (looked up on the first call per
+// device, then cached).
+constexpr int64_t kCeStaticRows = int64_t(1) << 18;
+hipError_t ce_static_scratch(float** rows);
+
 }  // namespace tpr

@@ -34,6 +34,7 @@
 // order (fp64 accumulation).
 #include <cstdlib>
 #include <cstring>
+#include <mutex>
 #include <type_traits>
 
 #include "common.h"
@@ -800,7 +801,35 @@ __global__ __launch_bounds__(1024) void loss_mean_kernel(const float* __restrict
 
 bool aligned16(const void* p) { return reinterpret_cast<uintptr_t>(p) % 16 == 0; }
 
+// The per-row losses of vocab_parallel_ce_fwd_bwd_noalloc(), for callers that
+// cannot allocate a workspace: one copy per device, held until the process
+// ends.  Every row kernel writes its row's entry before loss_mean_kernel
+// reads it, so nothing needs clearing between calls.
+static __device__ __align__(256) float scratch[kCeStaticRows];
+
 }  // namespace
+
+hipError_t ce_static_scratch(float** rows) {
+  constexpr int kMaxDev = 64;
+  static std::mutex mu;
+  static float* addr[kMaxDev];
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDev) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(mu);
+  if (addr[dev] == nullptr) {
+    // The array's device address on the current device (the name itself is
+    // only a host-side handle).
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (p == nullptr) return hipErrorInvalidSymbol;
+    addr[dev] = static_cast<float*>(p);
+  }
+  *rows = addr[dev];
+  return hipSuccess;
+}
 
 hipError_t launch_vocab_ce(const CeArgs& a, hipStream_t s) {
   CeOpt o{};

@@ -121,6 +121,16 @@ def test_partial_sum_rejects_bad_arguments(lib):
     assert f(2, 0, N, 0, N, N) == binding.TPR_OK                     # nothing to do, nothing enqueued
 
 
+def test_ce_noalloc_rejects_bad_arguments(lib):
+    f = lib.vocab_parallel_ce_fwd_bwd_noalloc
+    p = ctypes.c_void_p(16)  # never dereferenced: validation stops first
+    assert f(1, 1, 4, 8, N, N, N, N, N, N) == binding.TPR_ERR_NULLPTR
+    assert f(0, 1, 4, 8, p, p, p, p, N, N) == binding.TPR_ERR_PARTITION
+    assert f(2, 9, 4, 8, p, p, p, p, N, N) == binding.TPR_ERR_DTYPE
+    assert f(1, 1, (1 << 18) + 1, 8, p, p, p, p, N, N) == binding.TPR_ERR_WORKSPACE   # beyond the static array
+    assert b"static scratch" in lib.tprank_last_error()
+
+
 def test_head_ce_workspace_and_bad_arguments(lib):
     ws = lib.vocab_parallel_head_ce_workspace_bytes
     # logits + dlogits (bf16), row losses, and 8 fp32 partials of dh
