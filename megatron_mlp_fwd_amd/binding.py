@@ -14,7 +14,9 @@ import os
 import torch
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_PKG, "libtprank.so")
+# The in-tree library; TPRANK_LIB names another build of it (e.g. the
+# host-sanitized variant that build.build_host_asan() makes).
+LIB_PATH = os.environ.get("TPRANK_LIB") or os.path.join(_PKG, "libtprank.so")
 
 (TPR_OK, TPR_ERR_SHAPE, TPR_ERR_PARTITION, TPR_ERR_DTYPE, TPR_ERR_WORKSPACE, TPR_ERR_NULLPTR, TPR_ERR_HIP,
  TPR_ERR_VALUE) = range(8)

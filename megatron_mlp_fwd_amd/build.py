@@ -3,6 +3,12 @@
 Usage: ``python -m megatron_mlp_fwd_amd.build`` (or ``build()`` from Python).
 Every call recompiles every source; objects go to ``_build/`` (git-ignored),
 the library to ``megatron_mlp_fwd_amd/libtprank.so``.
+
+``build_host_asan()`` makes a variant for checking the host side: the C ABI's
+argument validation, shard planning and workspace carving (capi.cpp) built
+with AddressSanitizer on the host pass only, linked with the regular device
+objects, into ``_build/asan/libtprank.so``.  Load it with the sanitizer
+runtime preloaded (``ASAN_RUNTIME``) and ``TPRANK_LIB`` pointing at it.
 """
 import concurrent.futures as cf
 import os
@@ -54,6 +60,32 @@ def build(verbose=False):
         raise RuntimeError(f"link failed:\n{r.stderr}")
     shutil.move(tmp, OUT)
     return OUT
+
+
+ASAN_RUNTIME = "/opt/rocm/llvm/lib/clang/22/lib/linux/libclang_rt.asan-x86_64.so"
+
+
+def build_host_asan():
+    """Host-sanitized variant of the library (see the module docstring);
+    returns its path.  Builds the regular objects first when they are missing."""
+    if not all(os.path.exists(os.path.join(BUILD, os.path.splitext(s)[0] + ".o")) for s in SOURCES):
+        build()
+    out_dir = os.path.join(BUILD, "asan")
+    os.makedirs(out_dir, exist_ok=True)
+    obj = os.path.join(out_dir, "capi.o")
+    host_asan = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fno-omit-frame-pointer", "-g"]
+    cmd = [HIPCC, *FLAGS, *host_asan, "-x", "hip", "-c", os.path.join(CSRC, "capi.cpp"), "-o", obj]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"hipcc failed for capi.cpp (host ASan):\n{r.stderr}")
+    objs = [obj] + [os.path.join(BUILD, os.path.splitext(s)[0] + ".o") for s in SOURCES if s != "capi.cpp"]
+    lib = os.path.join(out_dir, "libtprank.so")
+    cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-Xarch_host", "-fsanitize=address",
+           "-shared-libasan", "-o", lib, *objs]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"link failed (host ASan):\n{r.stderr}")
+    return lib
 
 
 if __name__ == "__main__":

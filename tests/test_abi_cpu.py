@@ -220,3 +220,53 @@ def test_attn_proj_workspace_and_bad_arguments(lib):
     assert call(2, 8, 8, 4, dtype=5) == binding.TPR_ERR_DTYPE
     assert call(2, 8, 8, 4, layout=2) == binding.TPR_ERR_DTYPE
     assert call(2, 8, 8, 4, wsb=16) == binding.TPR_ERR_WORKSPACE
+
+
+def _no_gpu():
+    try:
+        import torch
+        return not torch.cuda.is_available()
+    except Exception:
+        return True
+
+
+@pytest.mark.skipif(not _no_gpu(), reason="walks the planner with placeholder pointers: only where no GPU is visible")
+def test_planner_runs_to_the_first_launch_without_a_device(lib):
+    # Valid sizes, 256-byte aligned placeholder pointers that the host never
+    # dereferences: each entry point validates, plans its shards, carves its
+    # workspace and builds its launches, then the first launch fails because
+    # there is no device (TPR_ERR_HIP).  Under the host-sanitized build this
+    # puts the whole planner, not only the error paths, under ASan.
+    p = ctypes.c_void_p(1 << 32)
+    big = 1 << 40
+    for axis in (0, 1, 2):
+        for dtype in (0, 1):
+            for M, K, N, parts in ((3, 5, 4, 2), (3, 5, 4, 7), (300, 136, 520, 3), (8192, 1024, 8192, 8)):
+                assert lib.sharded_matmul_fwd_bwd(axis, parts, dtype, M, K, N, p, p, p, p, p, p, p, big, N_) == \
+                    binding.TPR_ERR_HIP, (axis, dtype, M, K, N, parts)
+    for dtype in (0, 1):
+        for tp, T, d, f in ((1, 8192, 8192, 3584), (1, 4096, 4096, 1792), (3, 300, 264, 200), (300, 64, 40, 24)):
+            for layout in (0, 1):
+                assert lib.tp_mlp_fwd_bwd(tp, dtype, layout, T, d, f, *[p] * 8, p, big, N_) == binding.TPR_ERR_HIP
+                for act in (0, 1, 2):
+                    for w3 in (N_, p):
+                        assert lib.tp_mlp_act_fwd_bwd(tp, dtype, layout, act, T, d, f, p, p, w3, p, p, p, p, p, p, p,
+                                                      p, big, N_) == binding.TPR_ERR_HIP
+        for tp, hq, hkv, dh in ((1, 8, 1, 128), (2, 8, 2, 16), (8, 32, 8, 8)):
+            assert lib.tp_attn_proj_fwd_bwd(tp, dtype, 0, 272, 320, hq, hkv, dh, *[p] * 12, p, big, N_) == \
+                binding.TPR_ERR_HIP
+        for parts, T, V in ((8, 4096, 128256), (3, 5, 1001), (300, 4, 100), (4, 3, 8 * 11264 + 24)):
+            for stats in (N_, p):
+                assert lib.vocab_parallel_ce_fwd_bwd(parts, dtype, T, V, p, p, p, p, stats, p, big, N_) == \
+                    binding.TPR_ERR_HIP
+                assert lib.vocab_parallel_ce_fwd_bwd_noalloc(parts, dtype, T, V, p, p, p, p, stats, N_) == \
+                    binding.TPR_ERR_HIP
+                assert lib.vocab_parallel_ce_opts_fwd_bwd(parts, dtype, T, V, V - 3, -100, 0.1, p, p, p, p, stats, p,
+                                                          big, N_) == binding.TPR_ERR_HIP
+            for layout in (0, 1):
+                assert lib.vocab_parallel_head_ce_fwd_bwd(parts, dtype, layout, T, 64, V, p, p, p, p, p, p, p, big,
+                                                          N_) == binding.TPR_ERR_HIP
+    assert lib.tprank_partial_sum(8, 8192 * 8192, p, 8192 * 8192, ctypes.c_void_p(1 << 44), N_) == binding.TPR_ERR_HIP
+
+
+N_ = None
