@@ -216,7 +216,7 @@ bool aligned(const void* p, int bytes) { return (reinterpret_cast<uintptr_t>(p) 
 hipError_t launch_gemm_bf16(GemmBatch& b, bool a_kmajor, bool b_kmajor, int epi, hipStream_t s) {
   b.nxcd = device_topology().xcds;
   int total = 0;
-  bool vec = true, vec_c = true;
+  bool vec = true, vec_c = true, vec16 = true;
   for (int i = 0; i < b.count; ++i) {
     GemmProb& p = b.p[i];
     p.tiles_m = (p.M + BM - 1) / BM;
@@ -232,10 +232,12 @@ hipError_t launch_gemm_bf16(GemmBatch& b, bool a_kmajor, bool b_kmajor, int epi,
     const int cbytes = epi == EPI_F32 ? 16 : 8;
     vec_c = vec_c && aligned(p.C, cbytes) && p.ldc % 4 == 0 && (epi != EPI_ACT || aligned(p.aux_out, 8)) &&
             (epi != EPI_MUL || aligned(p.aux_in, 8));
+    vec16 = vec16 && epi != EPI_F32 && aligned(p.C, 16) && p.ldc % 8 == 0 &&
+            (epi != EPI_ACT || aligned(p.aux_out, 16)) && (epi != EPI_MUL || aligned(p.aux_in, 16));
   }
   b.total_tiles = total;
   if (total == 0) return hipSuccess;
-  const int vc = vec_c ? 1 : 0;
+  const int vc = (vec_c ? 1 : 0) | (vec_c && vec16 ? 2 : 0);
   if (a_kmajor && !b_kmajor) return vec ? launch_epi<true, false, true>(b, epi, vc, s) : launch_epi<true, false, false>(b, epi, vc, s);
   if (a_kmajor && b_kmajor) return vec ? launch_epi<true, true, true>(b, epi, vc, s) : launch_epi<true, true, false>(b, epi, vc, s);
   if (!a_kmajor && !b_kmajor) return vec ? launch_epi<false, false, true>(b, epi, vc, s) : launch_epi<false, false, false>(b, epi, vc, s);

@@ -428,6 +428,17 @@ bool gemm_bf16_dma_eligible(const GemmProb& p, bool a_kmajor, bool b_kmajor, int
   return a_bytes < limit && b_bytes < limit;
 }
 
+// Output vector widths a problem's epilogue may use: bit 0 for 16-byte fp32
+// or 8-byte bf16 vectors, bit 1 for 16-byte bf16 vectors (8 values).
+static int output_vectors(const GemmProb& p, int epi) {
+  const int cbytes = epi == EPI_F32 ? 16 : 8;
+  const bool v = aligned(p.C, cbytes) && p.ldc % 4 == 0 && (epi != EPI_ACT || aligned(p.aux_out, 8)) &&
+                 (epi != EPI_MUL || aligned(p.aux_in, 8));
+  const bool v16 = epi != EPI_F32 && aligned(p.C, 16) && p.ldc % 8 == 0 && (epi != EPI_ACT || aligned(p.aux_out, 16)) &&
+                   (epi != EPI_MUL || aligned(p.aux_in, 16));
+  return (v ? 1 : 0) | (v && v16 ? 2 : 0);
+}
+
 // Problems arrive with `kind` set; the launcher lays out the flattened grid
 // (each problem padded to a multiple of the device's XCD count) and records
 // whether each problem's outputs allow vector stores (kind bit 8).
@@ -442,10 +453,7 @@ hipError_t launch_gemm_bf16_dma(GemmBatch& b, hipStream_t s) {
     p.tiles_n = (p.N + BN - 1) / BN;
     p.tile_start = total;
     total += ((p.tiles_m * p.tiles_n + X - 1) / X) * X;
-    const int cbytes = epi == EPI_F32 ? 16 : 8;
-    const bool vec_c = aligned(p.C, cbytes) && p.ldc % 4 == 0 && (epi != EPI_ACT || aligned(p.aux_out, 8)) &&
-                       (epi != EPI_MUL || aligned(p.aux_in, 8));
-    p.kind = (p.kind & 0xff) | (vec_c ? 0x100 : 0);
+    p.kind = (p.kind & 0xff) | (output_vectors(p, epi) << 8);
   }
   b.total_tiles = total;
   if (total == 0) return hipSuccess;

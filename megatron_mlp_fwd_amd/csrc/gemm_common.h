@@ -134,6 +134,61 @@ __device__ __forceinline__ void epilogue_store(const GemmProb& P, floatx4 v, int
   }
 }
 
+// The bf16-output epilogues on eight consecutive outputs C[m][n .. n+7]
+// (a, b: columns n .. n+3 and n+4 .. n+7).  vec_c bit 1 allows one 16-byte
+// store per output (and, for EPI_MUL, `pre` holds the eight sigma'(P)
+// values); bit 0 allows 8-byte halves; otherwise element by element.
+template <int EPI, int ACT = ACT_GELU>
+__device__ __forceinline__ void epilogue_store8(const GemmProb& P, floatx4 a, floatx4 b, int64_t off, int n, int N,
+                                                int vec_c, u32x4 pre = u32x4{0u, 0u, 0u, 0u}) {
+  float v[8] = {a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+  const bool full16 = (vec_c & 2) && (n + 7 < N);
+  uint16_t* c = static_cast<uint16_t*>(P.C) + off;
+  float g[8];  // EPI_ACT: the activation (second output)
+  if constexpr (EPI == EPI_ACT) {
+#pragma unroll
+    for (int r = 0; r < 8; ++r) {
+      float s, ds;
+      act_fast<ACT>(v[r], s, ds);
+      g[r] = s;
+      v[r] = ds;
+    }
+  } else if constexpr (EPI == EPI_MUL) {
+    if (full16) {
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        v[2 * q] *= bf_lo(pre[q]);
+        v[2 * q + 1] *= bf_hi(pre[q]);
+      }
+    } else {
+      const uint16_t* p = static_cast<const uint16_t*>(P.aux_in) + off;
+#pragma unroll
+      for (int r = 0; r < 8; ++r)
+        if (n + r < N) v[r] *= __uint_as_float((uint32_t)p[r] << 16);
+    }
+  }
+  auto put = [&](uint16_t* dst, const float (&x)[8]) {
+    if (full16) {
+      *reinterpret_cast<u32x4*>(dst) =
+          u32x4{pack_bf16(x[0], x[1]), pack_bf16(x[2], x[3]), pack_bf16(x[4], x[5]), pack_bf16(x[6], x[7])};
+      return;
+    }
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      if ((vec_c & 1) && n + 4 * h + 3 < N) {
+        *reinterpret_cast<u32x2*>(dst + 4 * h) =
+            u32x2{pack_bf16(x[4 * h], x[4 * h + 1]), pack_bf16(x[4 * h + 2], x[4 * h + 3])};
+      } else {
+#pragma unroll
+        for (int r = 4 * h; r < 4 * h + 4; ++r)
+          if (n + r < N) dst[r] = __builtin_bit_cast(uint16_t, (__bf16)x[r]);
+      }
+    }
+  };
+  put(c, v);
+  if constexpr (EPI == EPI_ACT) put(static_cast<uint16_t*>(P.aux_out) + off, g);
+}
+
 // Epilogue through LDS (`stage` must be free and hold 32 * (TN_ + 4) floats per
 // wave).  Pass q moves MFMA blocks mi = 2q, 2q+1 of every wave (a 32 x TN_
 // region per wave) into LDS, then each wave reads its region back
@@ -145,28 +200,31 @@ template <int EPI, int TM_, int TN_, int ACT = ACT_GELU>
 __device__ __forceinline__ void epilogue_via_lds(float* stage, const floatx4 (&acc)[TN_ / 16][TM_ / 16],
                                                  const GemmProb& P, int m0, int n0, int wid, int wm, int wn,
                                                  int lane, int vec_c) {
+  // fp32 outputs: four columns (one 16-byte store) per lane; bf16 outputs:
+  // eight columns per lane, so each output is again one 16-byte store.
+  constexpr int CPL = EPI == EPI_F32 ? 4 : 8;
   constexpr int LD = TN_ + 4;
-  constexpr int LANES_PER_ROW = TN_ / 4;
+  constexpr int LANES_PER_ROW = TN_ / CPL;
   constexpr int ROWS_PER_IT = 64 / LANES_PER_ROW;
   constexpr int ITS = 32 / ROWS_PER_IT;
   float* ep = stage + wid * (32 * LD);
   const int64_t ldc = P.ldc;
   const int M = P.M, N = P.N;
-  const int col = 4 * (lane % LANES_PER_ROW);
+  const int col = CPL * (lane % LANES_PER_ROW);
   const int n = n0 + wn * TN_ + col;
-  const bool vec_n = vec_c && n + 3 < N;
   // For EPI_MUL the whole tile's sigma'(P) values (TM_/32 passes x ITS
   // loads per lane) are requested before the first pass, so their latency
   // overlaps the LDS exchanges instead of stalling each pass.
   constexpr int NPRE = EPI == EPI_MUL ? (TM_ / 32) * ITS : 1;
-  u32x2 pre[NPRE];
+  u32x4 pre[NPRE];
   if constexpr (EPI == EPI_MUL) {
+    const bool vec16 = (vec_c & 2) && n + 7 < N;
 #pragma unroll
     for (int i = 0; i < NPRE; ++i) {
       const int m = m0 + wm * TM_ + 32 * (i / ITS) + lane / LANES_PER_ROW + ROWS_PER_IT * (i % ITS);
-      pre[i] = (vec_n && m < M)
-                   ? *reinterpret_cast<const u32x2*>(static_cast<const uint16_t*>(P.aux_in) + (int64_t)m * ldc + n)
-                   : u32x2{0u, 0u};
+      pre[i] = (vec16 && m < M)
+                   ? *reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(P.aux_in) + (int64_t)m * ldc + n)
+                   : u32x4{0u, 0u, 0u, 0u};
     }
   }
   // Passes are unrolled at compile time (static_for), so acc and pre are
@@ -182,18 +240,23 @@ __device__ __forceinline__ void epilogue_via_lds(float* stage, const floatx4 (&a
             acc[ni][2 * q + h];
     __syncthreads();
     // All of the pass's LDS reads first (one wait), then the math and stores.
-    floatx4 vals[ITS];
+    floatx4 vals[ITS][CPL / 4];
 #pragma unroll
     for (int it = 0; it < ITS; ++it)
-      vals[it] = *reinterpret_cast<const floatx4*>(ep + (ROWS_PER_IT * it + lane / LANES_PER_ROW) * LD + col);
+#pragma unroll
+      for (int c4 = 0; c4 < CPL / 4; ++c4)
+        vals[it][c4] =
+            *reinterpret_cast<const floatx4*>(ep + (ROWS_PER_IT * it + lane / LANES_PER_ROW) * LD + col + 4 * c4);
 #pragma unroll
     for (int it = 0; it < ITS; ++it) {
       const int m = mbase + ROWS_PER_IT * it;
       if (m < M && n < N) {
-        if constexpr (EPI == EPI_MUL)
-          epilogue_store<EPI, ACT>(P, vals[it], (int64_t)m * ldc + n, n, N, vec_c, pre[q * ITS + it]);
+        if constexpr (EPI == EPI_F32)
+          epilogue_store<EPI, ACT>(P, vals[it][0], (int64_t)m * ldc + n, n, N, vec_c);
+        else if constexpr (EPI == EPI_MUL)
+          epilogue_store8<EPI, ACT>(P, vals[it][0], vals[it][1], (int64_t)m * ldc + n, n, N, vec_c, pre[q * ITS + it]);
         else
-          epilogue_store<EPI, ACT>(P, vals[it], (int64_t)m * ldc + n, n, N, vec_c);
+          epilogue_store8<EPI, ACT>(P, vals[it][0], vals[it][1], (int64_t)m * ldc + n, n, N, vec_c);
       }
     }
     __syncthreads();
