@@ -189,8 +189,17 @@ __device__ __forceinline__ void epilogue_store8(const GemmProb& P, floatx4 a, fl
   if constexpr (EPI == EPI_ACT) put(static_cast<uint16_t*>(P.aux_out) + off, g);
 }
 
+// Ordering point between one wave's LDS writes and its own lanes' reads (and
+// the next pass's writes): a wave's LDS instructions execute in program
+// order, so only the compiler must be kept from moving accesses across it.
+__device__ __forceinline__ void wave_sync() {
+  __builtin_amdgcn_wave_barrier();
+  asm volatile("" ::: "memory");
+}
+
 // Epilogue through LDS (`stage` must be free and hold 32 * (TN_ + 4) floats per
-// wave).  Pass q moves MFMA blocks mi = 2q, 2q+1 of every wave (a 32 x TN_
+// wave; each wave writes and reads back only its own region, so the passes
+// need no workgroup barrier, only the caller's one before the first pass).  Pass q moves MFMA blocks mi = 2q, 2q+1 of every wave (a 32 x TN_
 // region per wave) into LDS, then each wave reads its region back
 // row-contiguously and applies the epilogue with coalesced stores.  For
 // EPI_MUL the tile's sigma'(P) values are loaded before the first exchange.  The wave (wm, wn) owns rows wm*TM_ .. and
@@ -238,7 +247,7 @@ __device__ __forceinline__ void epilogue_via_lds(float* stage, const floatx4 (&a
       for (int ni = 0; ni < TN_ / 16; ++ni)
         *reinterpret_cast<floatx4*>(ep + (h * 16 + (lane & 15)) * LD + ni * 16 + 4 * (lane >> 4)) =
             acc[ni][2 * q + h];
-    __syncthreads();
+    wave_sync();
     // All of the pass's LDS reads first (one wait), then the math and stores.
     floatx4 vals[ITS][CPL / 4];
 #pragma unroll
@@ -259,7 +268,7 @@ __device__ __forceinline__ void epilogue_via_lds(float* stage, const floatx4 (&a
           epilogue_store8<EPI, ACT>(P, vals[it][0], vals[it][1], (int64_t)m * ldc + n, n, N, vec_c);
       }
     }
-    __syncthreads();
+    wave_sync();
   });
 }
 
