@@ -395,6 +395,14 @@ int mlp_plain(int tp, int dtype, bool math, int act, int64_t T, int64_t d, int64
   for (const Scale& c : scale)
     if ((he = tpr::launch_mul_f32_into(dtype, c.pre, c.dh, c.n, s)) != hipSuccess)
       return hip_fail(he, "dZ of the co-scheduled rows");
+  // With every row of dH computed in the fc1 launch, {fc2, dW2} and {dW1, dx}
+  // read nothing the other writes (dZ is complete after the product above),
+  // so they share one grouped launch: its short fc2 / dx tiles fill in behind
+  // the long dW2 / dW1 tiles instead of leaving two partly empty rounds.
+  if (T1 == T) {
+    mid.insert(mid.end(), last.begin(), last.end());
+    last.clear();
+  }
   if ((he = run_jobs(mid, dtype, s)) != hipSuccess) return hip_fail(he, "fc2 / dW2 / dH GEMMs");
   if ((he = run_jobs(last, dtype, s)) != hipSuccess) return hip_fail(he, "dW1 / dx GEMMs");
   // The block's one reduction each way: y = sum_r Z_r, dx = sum_r dx_r.
