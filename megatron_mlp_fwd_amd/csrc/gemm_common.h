@@ -69,68 +69,18 @@ __device__ __forceinline__ TileCoord locate_tile(const GemmBatch& batch) {
   return TileCoord{g, first_m + local % gsize, local / gsize};
 }
 
-// Apply the epilogue to four consecutive outputs C[m][n .. n+3] (off = m*ldc+n).
-// For EPI_MUL, `pre` holds the four bf16 values sigma'(P) when the caller
-// prefetched them (full vector rows); otherwise they are loaded here.
-template <int EPI, int ACT = ACT_GELU>
-__device__ __forceinline__ void epilogue_store(const GemmProb& P, floatx4 v, int64_t off, int n, int N, int vec_c,
-                                               u32x2 pre = u32x2{0u, 0u}) {
-  const bool full = vec_c && (n + 3 < N);
-  if constexpr (EPI == EPI_F32) {
-    // fp32 results are final outputs, not read again by the kernels of the
-    // same call: non-temporal stores keep them from displacing the operand
-    // panels that the running tiles share in L2.
-    float* c = static_cast<float*>(P.C) + off;
-    if (full) {
-      __builtin_nontemporal_store(v, reinterpret_cast<floatx4*>(c));
-    } else {
-      for (int r = 0; r < 4; ++r)
-        if (n + r < N) __builtin_nontemporal_store(v[r], c + r);
-    }
-  } else if constexpr (EPI == EPI_ACT) {
-    // acc is the pre-activation P: the activation H = sigma(P) is the next
-    // GEMM's operand and sigma'(P), evaluated here from the fp32 accumulator,
-    // is all the backward pass needs of P.
-    uint16_t* c = static_cast<uint16_t*>(P.C) + off;
-    uint16_t* h = static_cast<uint16_t*>(P.aux_out) + off;
-    floatx4 gv, dv;
-    for (int r = 0; r < 4; ++r) {
-      float a, da;
-      act_fast<ACT>(v[r], a, da);
-      gv[r] = a;
-      dv[r] = da;
-    }
-    if (full) {
-      *reinterpret_cast<u32x2*>(c) = u32x2{pack_bf16(dv[0], dv[1]), pack_bf16(dv[2], dv[3])};
-      *reinterpret_cast<u32x2*>(h) = u32x2{pack_bf16(gv[0], gv[1]), pack_bf16(gv[2], gv[3])};
-    } else {
-      for (int r = 0; r < 4; ++r)
-        if (n + r < N) {
-          c[r] = __builtin_bit_cast(uint16_t, (__bf16)dv[r]);
-          h[r] = __builtin_bit_cast(uint16_t, (__bf16)gv[r]);
-        }
-    }
-  } else if constexpr (EPI == EPI_BF16) {
-    uint16_t* c = static_cast<uint16_t*>(P.C) + off;
-    if (full) {
-      *reinterpret_cast<u32x2*>(c) = u32x2{pack_bf16(v[0], v[1]), pack_bf16(v[2], v[3])};
-    } else {
-      for (int r = 0; r < 4; ++r)
-        if (n + r < N) c[r] = __builtin_bit_cast(uint16_t, (__bf16)v[r]);
-    }
-  } else {  // EPI_MUL: C = acc * sigma'(P), sigma'(P) read from aux_in (may alias C)
-    uint16_t* c = static_cast<uint16_t*>(P.C) + off;
-    if (full) {
-      v[0] *= bf_lo(pre[0]);
-      v[1] *= bf_hi(pre[0]);
-      v[2] *= bf_lo(pre[1]);
-      v[3] *= bf_hi(pre[1]);
-      *reinterpret_cast<u32x2*>(c) = u32x2{pack_bf16(v[0], v[1]), pack_bf16(v[2], v[3])};
-    } else {
-      const uint16_t* p = static_cast<const uint16_t*>(P.aux_in) + off;
-      for (int r = 0; r < 4; ++r)
-        if (n + r < N) c[r] = __builtin_bit_cast(uint16_t, (__bf16)(v[r] * __uint_as_float((uint32_t)p[r] << 16)));
-    }
+// The fp32 epilogue on four consecutive outputs C[m][n .. n+3] (off =
+// m*ldc+n): one 16-byte store when vec_c allows it and the row has room,
+// else element by element.  fp32 results are final outputs, not read again
+// by the kernels of the same call: non-temporal stores keep them from
+// displacing the operand panels that the running tiles share in L2.
+__device__ __forceinline__ void store_f32x4(const GemmProb& P, floatx4 v, int64_t off, int n, int N, int vec_c) {
+  float* c = static_cast<float*>(P.C) + off;
+  if (vec_c && n + 3 < N) {
+    __builtin_nontemporal_store(v, reinterpret_cast<floatx4*>(c));
+  } else {
+    for (int r = 0; r < 4; ++r)
+      if (n + r < N) __builtin_nontemporal_store(v[r], c + r);
   }
 }
 
@@ -261,7 +211,7 @@ __device__ __forceinline__ void epilogue_via_lds(float* stage, const floatx4 (&a
       const int m = mbase + ROWS_PER_IT * it;
       if (m < M && n < N) {
         if constexpr (EPI == EPI_F32)
-          epilogue_store<EPI, ACT>(P, vals[it][0], (int64_t)m * ldc + n, n, N, vec_c);
+          store_f32x4(P, vals[it][0], (int64_t)m * ldc + n, n, N, vec_c);
         else if constexpr (EPI == EPI_MUL)
           epilogue_store8<EPI, ACT>(P, vals[it][0], vals[it][1], (int64_t)m * ldc + n, n, N, vec_c, pre[q * ITS + it]);
         else
