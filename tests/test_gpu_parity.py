@@ -320,6 +320,25 @@ def test_mlp_bf16_tiles_and_tails(tpr, shape, tp, layout, gemm_path):
         assert e <= TOL_BF16, (name, e)
 
 
+@pytest.mark.parametrize("tp,shape", [(5, (300, 264, 200)), (8, (256, 128, 512)), (8, (96, 64, 40)),
+                                      (13, (130, 72, 9))])
+def test_mlp_bf16_many_ranks(tpr, tp, shape):
+    # More ranks than one grouped launch holds problems (16): the backward
+    # products of all ranks are then split over several launches, and with
+    # f < tp some ranks hold no hidden units.  Outputs start as NaN, so a
+    # product that no launch ran fails.
+    T, d, f = shape
+    say("TP MLP bf16 many ranks", tp, shape)
+    x, w1, w2, gy = workloads.rank_mlp(T, d, f, seed=tp * 31 + T, device=DEV, w_std=0.05)
+    out = _nan_out((T, d), (T, d), (d, f), (f, d))
+    got = tpr.tp_mlp_fwd_bwd(tp, x, w1, w2, gy, "math", out=out)
+    torch.cuda.synchronize()
+    want = oracle.mlp_fwd_bwd(f64(x), f64(w1), f64(w2), f64(gy), "math")
+    for name, w, o in zip(("y", "dx", "dw1", "dw2"), want, got):
+        e = rel_err(f64(o), w)
+        assert e <= TOL_BF16, (name, e)
+
+
 def test_mlp_zero_sizes(tpr):
     for T, d, f in ((0, 8, 8), (8, 8, 0), (8, 0, 8)):
         for dtype in (torch.float32, torch.bfloat16):
