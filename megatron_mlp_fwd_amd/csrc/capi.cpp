@@ -280,15 +280,17 @@ namespace {
 
 constexpr int kTile = 256;   // block tile of the bf16 GEMM
 
-// Rows of dH = gy W2^T computed in the fc1 launch of the plain bf16 MLP: T
-// (all of it) or 0.  fc1 fills sum_r ceil(T/256) ceil(f_r/256) tiles of
-// K = d; when its last round leaves enough compute units idle for every dH
-// tile (same K), dH runs there instead of in the next launch.  Moving only
-// some leading row blocks measured no gain (the fc1 launch grew by what the
-// next one lost, plus the separate multiply).  GELU only: the kernel
-// instance for other activations takes activation epilogues alone.
-int64_t cosched_rows(int dtype, int act, int tp, int64_t T, int64_t f) {
-  if (dtype != TPR_BF16 || act != TPR_ACT_GELU || T <= 0) return 0;
+// Whether dH = gy W2^T joins the fc1 launch of the plain bf16 MLP.  fc1
+// fills sum_r ceil(T/256) ceil(f_r/256) tiles of K = d; when its last round
+// leaves enough compute units idle for every dH tile (same K), dH runs there
+// instead of in the next launch.  fc1 then writes P in fp32 and one
+// element-wise pass forms H = sigma(P) and dZ = dH * sigma'(P) from the two
+// fp32 tiles, so no activation epilogue sits on the launch's critical path.
+// Moving only some leading row blocks of dH measured no gain (the fc1 launch
+// grew by what the next one lost, plus the separate multiply), so it is all
+// of dH or none.
+bool cosched_dh(int dtype, int tp, int64_t T, int64_t f) {
+  if (dtype != TPR_BF16 || T <= 0) return false;
   const int64_t tiles_m = (T + kTile - 1) / kTile;
   int64_t n1 = 0, nb = 0;
   for (int r = 0; r < tp; ++r) {
@@ -298,17 +300,18 @@ int64_t cosched_rows(int dtype, int act, int tp, int64_t T, int64_t f) {
     n1 += tiles_m * tn;
     nb += tn;
   }
-  if (nb == 0) return 0;
+  if (nb == 0) return false;
   const int64_t cus = tpr::device_topology().cus;
   const int64_t free = (cus - n1 % cus) % cus;
-  return (free / nb) * kTile >= T ? T : 0;
+  return (free / nb) * kTile >= T;
 }
 
 size_t mlp_workspace(int tp, int dtype, bool gated, int64_t T, int64_t d, int64_t f) {
   if (tp < 1 || !dtype_ok(dtype) || T < 0 || d < 0 || f < 0) return 0;
   const size_t tf = align256((size_t)(T * f * esize(dtype))), td = align256((size_t)(T * d * 4));
-  if (!gated)  // sigma'(P) / dZ, H, partials, fp32 dH of the co-scheduled rows
-    return 2 * tf + (tp > 1 ? 2 * (size_t)tp * td : 0) + align256((size_t)(cosched_rows(dtype, TPR_ACT_GELU, tp, T, f) * f * 4));
+  if (!gated)  // sigma'(P) / dZ, H, partials; with dH beside fc1, fp32 dH and fp32 P
+    return 2 * tf + (tp > 1 ? 2 * (size_t)tp * td : 0) +
+           (cosched_dh(dtype, tp, T, f) ? 2 * align256((size_t)(T * f * 4)) : 0);
   // gate, up, H; [dA | dU] per rank (dH first); [W1_r | W3_r] per rank; y and dx partials when tp > 1
   return 5 * tf + align256((size_t)(d * 2 * f * esize(dtype))) + (tp > 1 ? 2 * (size_t)tp * td : 0);
 }
@@ -322,7 +325,11 @@ int check_act(int act) {
 // Plain MLP: fc1's epilogue writes H = sigma(P) and sigma'(P) from the fp32
 // accumulator; then fc2 (row-parallel) with the two backward products that
 // need only H and gy: dW2 and dZ = (gy W2^T) * sigma'(P) (in place over
-// sigma'(P)); then dW1 and dx.
+// sigma'(P)); then dW1 and dx.  When dH joins the fc1 launch (cosched_dh),
+// fc1 and dH write fp32 P and dH, one element-wise pass forms H and dZ, and
+// fc2, dW2, dW1 and dx share the next launch: with dZ complete none of them
+// reads what another writes, and the short fc2 / dx tiles fill in behind the
+// long dW2 / dW1 tiles instead of leaving two partly empty rounds.
 int mlp_plain(int tp, int dtype, bool math, int act, int64_t T, int64_t d, int64_t f, const void* x, const void* w1,
               const void* w2, const void* gy, float* y, float* dx, float* dw1, float* dw2, void* ws, hipStream_t s) {
   const int64_t e = esize(dtype);
@@ -332,18 +339,14 @@ int mlp_plain(int tp, int dtype, bool math, int act, int64_t T, int64_t d, int64
   const int64_t pstride = (int64_t)(align256((size_t)(T * d * 4)) / 4);
   float* zpart = reinterpret_cast<float*>(wsb + 2 * align256((size_t)(T * f * e)));
   float* xpart = zpart + (int64_t)tp * pstride;
-  const int64_t T1 = cosched_rows(dtype, act, tp, T, f);  // dH rows [0, T1) join the fc1 launch
-  float* dh1 = reinterpret_cast<float*>(wsb + 2 * align256((size_t)(T * f * e)) +
-                                        (tp > 1 ? 2 * (size_t)tp * align256((size_t)(T * d * 4)) : 0));
+  const bool co = cosched_dh(dtype, tp, T, f);
+  // With dH beside fc1: T x f fp32 dH, then T x f fp32 P (rank blocks T x f_r).
+  float* dh32 = reinterpret_cast<float*>(wsb + 2 * align256((size_t)(T * f * e)) +
+                                         (tp > 1 ? 2 * (size_t)tp * align256((size_t)(T * d * 4)) : 0));
+  float* p32 = dh32 + align256((size_t)(T * f * 4)) / 4;
   const bool direct = tp == 1;
   int nslots = 0;
-  std::vector<Job> fwd1, mid, last;  // launch groups: fc1 (+ dH rows < T1) | fc2, dW2, dH | dW1, dx
-  struct Scale {
-    char* pre;        // sigma'(P) of rows < T1, becomes dZ
-    const float* dh;  // their fp32 dH
-    int64_t n;        // T1 * f_r elements
-  };
-  std::vector<Scale> scale;
+  std::vector<Job> fwd1, mid, last;  // launch groups: fc1 (+ dH) | fc2, dW2 (+ dH) | dW1, dx
   for (int r = 0; r < tp; ++r) {
     int64_t lo, hi;
     shard_of(f, tp, r, &lo, &hi);
@@ -355,51 +358,43 @@ int mlp_plain(int tp, int dtype, bool math, int act, int64_t T, int64_t d, int64
     float* xdst = direct ? dx : xpart + nslots * pstride;
     tpr::GemmProb p1;
     if (math) {  // w1 d x f, w2 f x d
-      p1 = prob(x, d, 1, cb(w1) + lo * e, f, 1, Pr, fr, T, fr, d, nullptr, Hr);
+      p1 = co ? prob(x, d, 1, cb(w1) + lo * e, f, 1, p32 + T * lo, fr, T, fr, d)
+              : prob(x, d, 1, cb(w1) + lo * e, f, 1, Pr, fr, T, fr, d, nullptr, Hr);
       p1.act = act;
-      fwd1.push_back(job(p1, true, false, tpr::EPI_ACT));
+      fwd1.push_back(job(p1, true, false, co ? tpr::EPI_F32 : tpr::EPI_ACT));
       mid.push_back(job(prob(Hr, fr, 1, cb(w2) + lo * d * e, d, 1, ydst, d, T, d, fr), true, false, tpr::EPI_F32));
       mid.push_back(job(prob(Hr, 1, fr, gy, d, 1, dw2 + lo * d, d, fr, d, T), false, false, tpr::EPI_F32));
-      if (T1 > 0)
-        fwd1.push_back(job(prob(gy, d, 1, cb(w2) + lo * d * e, 1, d, dh1 + T1 * lo, fr, T1, fr, d), true, true,
+      if (co)
+        fwd1.push_back(job(prob(gy, d, 1, cb(w2) + lo * d * e, 1, d, dh32 + T * lo, fr, T, fr, d), true, true,
                            tpr::EPI_F32));
-      if (T1 < T)
-        mid.push_back(job(prob(cb(gy) + T1 * d * e, d, 1, cb(w2) + lo * d * e, 1, d, Pr + T1 * fr * e, fr, T - T1, fr,
-                               d, Pr + T1 * fr * e), true, true, tpr::EPI_MUL));
+      else
+        mid.push_back(job(prob(gy, d, 1, cb(w2) + lo * d * e, 1, d, Pr, fr, T, fr, d, Pr), true, true, tpr::EPI_MUL));
       last.push_back(job(prob(x, 1, d, Pr, fr, 1, dw1 + lo, f, d, fr, T), false, false, tpr::EPI_F32));
       last.push_back(job(prob(Pr, fr, 1, cb(w1) + lo * e, 1, f, xdst, d, T, d, fr), true, true, tpr::EPI_F32));
     } else {  // w1 (f, d), w2 (d, f)
-      p1 = prob(x, d, 1, cb(w1) + lo * d * e, 1, d, Pr, fr, T, fr, d, nullptr, Hr);
+      p1 = co ? prob(x, d, 1, cb(w1) + lo * d * e, 1, d, p32 + T * lo, fr, T, fr, d)
+              : prob(x, d, 1, cb(w1) + lo * d * e, 1, d, Pr, fr, T, fr, d, nullptr, Hr);
       p1.act = act;
-      fwd1.push_back(job(p1, true, true, tpr::EPI_ACT));
+      fwd1.push_back(job(p1, true, true, co ? tpr::EPI_F32 : tpr::EPI_ACT));
       mid.push_back(job(prob(Hr, fr, 1, cb(w2) + lo * e, 1, f, ydst, d, T, d, fr), true, true, tpr::EPI_F32));
       mid.push_back(job(prob(gy, 1, d, Hr, fr, 1, dw2 + lo, f, d, fr, T), false, false, tpr::EPI_F32));
-      if (T1 > 0)
-        fwd1.push_back(job(prob(gy, d, 1, cb(w2) + lo * e, f, 1, dh1 + T1 * lo, fr, T1, fr, d), true, false,
+      if (co)
+        fwd1.push_back(job(prob(gy, d, 1, cb(w2) + lo * e, f, 1, dh32 + T * lo, fr, T, fr, d), true, false,
                            tpr::EPI_F32));
-      if (T1 < T)
-        mid.push_back(job(prob(cb(gy) + T1 * d * e, d, 1, cb(w2) + lo * e, f, 1, Pr + T1 * fr * e, fr, T - T1, fr, d,
-                               Pr + T1 * fr * e), true, false, tpr::EPI_MUL));
+      else
+        mid.push_back(job(prob(gy, d, 1, cb(w2) + lo * e, f, 1, Pr, fr, T, fr, d, Pr), true, false, tpr::EPI_MUL));
       last.push_back(job(prob(Pr, 1, fr, x, d, 1, dw1 + lo * d, d, fr, d, T), false, false, tpr::EPI_F32));
       last.push_back(job(prob(Pr, fr, 1, cb(w1) + lo * d * e, d, 1, xdst, d, T, d, fr), true, false, tpr::EPI_F32));
     }
-    if (T1 > 0 && T1 < T) scale.push_back(Scale{Pr, dh1 + T1 * lo, T1 * fr});
     ++nslots;
   }
   hipError_t he;
   if ((he = run_jobs(fwd1, dtype, s)) != hipSuccess) return hip_fail(he, "fc1 GEMM");
-  // dZ = dH * sigma'(P) for the rows whose dH ran with fc1 (fr columns each;
-  // the first T1 rows of a rank's block are its first T1 fr elements, and
-  // with T1 == T the ranks' blocks tile both buffers whole).
-  if (T1 == T && T > 0) scale.push_back(Scale{pre, dh1, T * f});
-  for (const Scale& c : scale)
-    if ((he = tpr::launch_mul_f32_into(dtype, c.pre, c.dh, c.n, s)) != hipSuccess)
-      return hip_fail(he, "dZ of the co-scheduled rows");
-  // With every row of dH computed in the fc1 launch, {fc2, dW2} and {dW1, dx}
-  // read nothing the other writes (dZ is complete after the product above),
-  // so they share one grouped launch: its short fc2 / dx tiles fill in behind
-  // the long dW2 / dW1 tiles instead of leaving two partly empty rounds.
-  if (T1 == T) {
+  if (co) {
+    // H = sigma(P) and dZ = dH * sigma'(P); the rank blocks of P, dH, H and
+    // dZ sit at the same element offsets (T * lo), so one pass covers all.
+    if ((he = tpr::launch_act_mul(p32, dh32, actv, pre, T * f, act, s)) != hipSuccess)
+      return hip_fail(he, "activation and dZ");
     mid.insert(mid.end(), last.begin(), last.end());
     last.clear();
   }

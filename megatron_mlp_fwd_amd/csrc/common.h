@@ -90,9 +90,9 @@ hipError_t launch_glu_bwd_2d(int dtype, void* dA, const void* A, const void* U, 
 // Copy rows x row_bytes from src (rows ld_src bytes apart) to dst (ld_dst).
 hipError_t launch_copy_2d(void* dst, int64_t ld_dst, const void* src, int64_t ld_src, int64_t rows, int64_t row_bytes,
                           hipStream_t s);
-// dst = dst * src over n contiguous elements: dst in `dtype` (16-byte
-// aligned), src fp32; the product is rounded once to `dtype`.
-hipError_t launch_mul_f32_into(int dtype, void* dst, const float* src, int64_t n, hipStream_t s);
+// H = sigma(P) and dZ = dH * sigma'(P) over n contiguous elements (act is
+// an Activation): P and dH fp32, H and dZ bf16, each rounded once.
+hipError_t launch_act_mul(const float* P, const float* dH, void* H, void* dZ, int64_t n, int act, hipStream_t s);
 
 // ---------------------------------------------------------------- vocab CE
 struct CeArgs {

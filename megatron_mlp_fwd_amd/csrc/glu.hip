@@ -143,38 +143,40 @@ __global__ __launch_bounds__(256) void glu_bwd_f32(float* __restrict__ dA, const
   }
 }
 
-// dst = bf16(dst * src), src fp32: the gradient at the pre-activation for
-// rows whose dH (fp32) was computed apart from the sigma'(P) it multiplies.
-__global__ __launch_bounds__(256) void mul_f32_into_bf16(uint16_t* __restrict__ dst, const float* __restrict__ src,
-                                                         int64_t n) {
-  const int64_t nv = n / 8;
+// The plain MLP's activation when dH = gy W2^T ran beside fc1 (TP lesson,
+// 2.A steps 2-3, and the multi-card page's 02 / BACKWARD rule G_Z = G_H *
+// sigma'): H = sigma(P) and dZ = dH * sigma'(P), from the fp32 P and dH tiles
+// of that launch, each rounded once to bf16.  VEC: 8 elements per thread
+// (16-byte aligned bases), then a scalar tail of n % 8.
+template <int ACT, bool VEC>
+__global__ __launch_bounds__(256) void act_mul_kernel(const float* __restrict__ P, const float* __restrict__ dH,
+                                                      uint16_t* __restrict__ H, uint16_t* __restrict__ dZ,
+                                                      int64_t n) {
   const int64_t stride = (int64_t)gridDim.x * blockDim.x;
-  for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < nv; i += stride) {
-    const u32x4 p = reinterpret_cast<const u32x4*>(dst)[i];
-    const f32x4 a = reinterpret_cast<const f32x4*>(src)[2 * i];
-    const f32x4 b = reinterpret_cast<const f32x4*>(src)[2 * i + 1];
-    u32x4 o;
-    o[0] = pack2(a[0] * bf_lo(p[0]), a[1] * bf_hi(p[0]));
-    o[1] = pack2(a[2] * bf_lo(p[1]), a[3] * bf_hi(p[1]));
-    o[2] = pack2(b[0] * bf_lo(p[2]), b[1] * bf_hi(p[2]));
-    o[3] = pack2(b[2] * bf_lo(p[3]), b[3] * bf_hi(p[3]));
-    reinterpret_cast<u32x4*>(dst)[i] = o;
+  const int64_t tid = blockIdx.x * (int64_t)blockDim.x + threadIdx.x;
+  const int64_t nv = VEC ? n / 8 : 0;
+  for (int64_t i = tid; i < nv; i += stride) {
+    const f32x4 p0 = reinterpret_cast<const f32x4*>(P)[2 * i], p1 = reinterpret_cast<const f32x4*>(P)[2 * i + 1];
+    const f32x4 g0 = reinterpret_cast<const f32x4*>(dH)[2 * i], g1 = reinterpret_cast<const f32x4*>(dH)[2 * i + 1];
+    const float p[8] = {p0[0], p0[1], p0[2], p0[3], p1[0], p1[1], p1[2], p1[3]};
+    const float g[8] = {g0[0], g0[1], g0[2], g0[3], g1[0], g1[1], g1[2], g1[3]};
+    float h[8], z[8];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      float sv, ds;
+      act_fast<ACT>(p[k], sv, ds);
+      h[k] = sv;
+      z[k] = g[k] * ds;
+    }
+    reinterpret_cast<u32x4*>(H)[i] = u32x4{pack2(h[0], h[1]), pack2(h[2], h[3]), pack2(h[4], h[5]), pack2(h[6], h[7])};
+    reinterpret_cast<u32x4*>(dZ)[i] = u32x4{pack2(z[0], z[1]), pack2(z[2], z[3]), pack2(z[4], z[5]), pack2(z[6], z[7])};
   }
-  const int64_t t = 8 * nv + blockIdx.x * (int64_t)blockDim.x + threadIdx.x;
-  if (t < n) dst[t] = to_bf(src[t] * bf(dst[t]));
-}
-
-__global__ __launch_bounds__(256) void mul_f32_into_bf16_scalar(uint16_t* __restrict__ dst,
-                                                                const float* __restrict__ src, int64_t n) {
-  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
-  for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < n; i += stride)
-    dst[i] = to_bf(src[i] * bf(dst[i]));
-}
-
-__global__ __launch_bounds__(256) void mul_f32_into_f32(float* __restrict__ dst, const float* __restrict__ src,
-                                                        int64_t n) {
-  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
-  for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < n; i += stride) dst[i] *= src[i];
+  for (int64_t t = 8 * nv + tid; t < n; t += stride) {
+    float sv, ds;
+    act_fast<ACT>(P[t], sv, ds);
+    H[t] = to_bf(sv);
+    dZ[t] = to_bf(dH[t] * ds);
+  }
 }
 
 // dA / dU of a rows x cols block: dH and the outputs rows `ld` apart, A and
@@ -311,16 +313,23 @@ hipError_t launch_copy_2d(void* dst, int64_t ld_dst, const void* src, int64_t ld
   return hipGetLastError();
 }
 
-hipError_t launch_mul_f32_into(int dtype, void* dst, const float* src, int64_t n, hipStream_t s) {
+hipError_t launch_act_mul(const float* P, const float* dH, void* H, void* dZ, int64_t n, int act, hipStream_t s) {
   if (n <= 0) return hipSuccess;
-  const bool vec = reinterpret_cast<uintptr_t>(dst) % 16 == 0 && reinterpret_cast<uintptr_t>(src) % 16 == 0;
-  if (dtype == 1 && vec)
-    hipLaunchKernelGGL(mul_f32_into_bf16, dim3(grid_for(n / 8)), dim3(256), 0, s, static_cast<uint16_t*>(dst), src, n);
-  else if (dtype == 1)
-    hipLaunchKernelGGL(mul_f32_into_bf16_scalar, dim3(grid_for(n)), dim3(256), 0, s, static_cast<uint16_t*>(dst), src,
-                       n);
-  else
-    hipLaunchKernelGGL(mul_f32_into_f32, dim3(grid_for(n)), dim3(256), 0, s, static_cast<float*>(dst), src, n);
+  const bool vec = reinterpret_cast<uintptr_t>(P) % 16 == 0 && reinterpret_cast<uintptr_t>(dH) % 16 == 0 &&
+                   reinterpret_cast<uintptr_t>(H) % 16 == 0 && reinterpret_cast<uintptr_t>(dZ) % 16 == 0;
+  uint16_t* h = static_cast<uint16_t*>(H);
+  uint16_t* z = static_cast<uint16_t*>(dZ);
+  const dim3 grid(grid_for(vec ? n / 8 : n)), block(256);
+  if (act == ACT_TANH) {
+    if (vec) hipLaunchKernelGGL((act_mul_kernel<ACT_TANH, true>), grid, block, 0, s, P, dH, h, z, n);
+    else hipLaunchKernelGGL((act_mul_kernel<ACT_TANH, false>), grid, block, 0, s, P, dH, h, z, n);
+  } else if (act == ACT_SILU) {
+    if (vec) hipLaunchKernelGGL((act_mul_kernel<ACT_SILU, true>), grid, block, 0, s, P, dH, h, z, n);
+    else hipLaunchKernelGGL((act_mul_kernel<ACT_SILU, false>), grid, block, 0, s, P, dH, h, z, n);
+  } else {
+    if (vec) hipLaunchKernelGGL((act_mul_kernel<ACT_GELU, true>), grid, block, 0, s, P, dH, h, z, n);
+    else hipLaunchKernelGGL((act_mul_kernel<ACT_GELU, false>), grid, block, 0, s, P, dH, h, z, n);
+  }
   return hipGetLastError();
 }
 

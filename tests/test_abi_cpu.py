@@ -71,8 +71,8 @@ def test_workspace_sizes(lib):
     assert lib.sharded_matmul_workspace_bytes(3, 2, 0, 3, 5, 4) == 0            # invalid axis
     # bf16: sigma'(P) / dZ and H; 448 fc1 tiles leave 64 compute units free, too few for dH's 448
     assert lib.tp_mlp_workspace_bytes(1, 1, 8192, 8192, 3584) == 2 * 8192 * 3584 * 2
-    # 8B rank: 112 fc1 tiles leave room for all 112 dH tiles, kept in fp32 (T x f)
-    assert lib.tp_mlp_workspace_bytes(1, 1, 4096, 4096, 1792) == 2 * 4096 * 1792 * 2 + 4096 * 1792 * 4
+    # 8B rank: 112 fc1 tiles leave room for all 112 dH tiles; fc1's P and dH kept in fp32 (T x f each)
+    assert lib.tp_mlp_workspace_bytes(1, 1, 4096, 4096, 1792) == 2 * 4096 * 1792 * 2 + 2 * 4096 * 1792 * 4
     assert lib.tp_mlp_workspace_bytes(4, 0, 16, 64, 256) == 2 * 16 * 256 * 4 + 2 * 4 * 16 * 64 * 4
     assert lib.vocab_parallel_ce_workspace_bytes(8, 4096, 128256) == 4096 * 4
 

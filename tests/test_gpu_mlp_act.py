@@ -79,6 +79,28 @@ def test_mlp_act(tpr, dtype, act, gated, layout, tp):
         assert e <= tol, (name, e)
 
 
+@pytest.mark.parametrize("tp", [1, 3])
+@pytest.mark.parametrize("layout", ["math", "torch"])
+@pytest.mark.parametrize("act", ["gelu", "tanh", "silu"])
+def test_mlp_act_bf16_fc1_fills_the_chip(tpr, act, layout, tp):
+    # T = 1024, f = 16384: fc1 alone fills whole rounds of the 256 compute
+    # units (tp 1: 4 x 64 = 256 tiles; tp 3: 4 x 66 = 264 tiles, whose second
+    # round leaves room for 3 of dH's 4 row blocks only), so dH does not join
+    # the fc1 launch: fc1 takes the activation epilogue (sigma and sigma' from
+    # the accumulator) and dH the multiplying one.  The smaller shapes above
+    # take the other schedule (fp32 P and dH, then one element-wise pass).
+    T, d, f = 1024, 128, 16384
+    say("MLP bf16, fc1 fills the chip", act, layout, "tp", tp, (T, d, f))
+    x, _, _, gy = workloads.rank_mlp(T, d, 8, seed=T + tp, device=DEV, dtype=torch.bfloat16)
+    w1, w2, w3 = _weights(d, f, seed=11 * tp, dtype=torch.bfloat16, layout=layout, gated=False, std=0.05)
+    got = tpr.tp_mlp_act_fwd_bwd(tp, x, w1, w2, gy, act=act, w_layout=layout)
+    torch.cuda.synchronize()
+    want = mlp_act_fwd_bwd(f64(x), f64(w1), f64(w2), f64(gy), act, None, layout)
+    for name, g, w in zip(("y", "dx", "dw1", "dw2"), got, want):
+        e = rel_err(f64(g), w)
+        assert e <= 2e-2, (name, e)
+
+
 def test_gelu_act_matches_plain_entry_point(tpr):
     say("tp_mlp_act gelu == tp_mlp_fwd_bwd")
     x, w1, w2, gy = workloads.rank_mlp(300, 264, 200, seed=4, device=DEV)
