@@ -146,8 +146,9 @@ int tprank_partial_sum(int nslots, int64_t n, const float* partials, int64_t slo
  * and the activation (T x f each, in `dtype`; the first buffer is reused for
  * the gradient at the pre-activation), plus, when tp > 1, the tp full-shape
  * fp32 partials of y and of dx, plus (TPR_BF16, when gy W2^T fits in the
- * idle compute units of the forward launch's last round) that product in
- * fp32 (T x f).  Returns 0 for invalid arguments.
+ * idle compute units of the forward launch's last round) that product and
+ * the pre-activation, both in fp32 (T x f each).  Returns 0 for invalid
+ * arguments.
  */
 size_t tp_mlp_workspace_bytes(int tp, int dtype, int64_t T, int64_t d, int64_t f);
 
@@ -163,13 +164,14 @@ size_t tp_mlp_workspace_bytes(int tp, int dtype, int64_t T, int64_t d, int64_t f
  * then y = sum_r Z_r and dx = sum_r dx_r (the MLP's one reduction each way,
  * fixed rank order).  For TPR_BF16, when the forward launch leaves enough
  * compute units idle, gy W2_r^T is computed alongside P_r (it does not
- * depend on it), kept in fp32 and multiplied by gelu'(P_r) afterwards (one
- * rounding, as in the fused epilogue otherwise used).  With tp == 1 the call
+ * depend on it); both are kept in fp32 and one element-wise pass forms H_r
+ * and dZ_r from them, each rounded once (no rounded gelu' in between).
+ * With tp == 1 the call
  * computes one rank's share: pass
  * the rank's weight shards (w1 d x f_r, w2 f_r x d in TPR_W_MATH) and y, dx
  * are that rank's partials Z_r, dx_r.  For TPR_BF16 the activation and the
  * pre-activation gradient are rounded to bf16 (they are GEMM operands), and
- * so is the kept gelu'(P_r).
+ * so is the kept gelu'(P_r) of the fused-epilogue schedule.
  *   x, gy: T x d in `dtype` (leading dims of an activation flatten into T);
  *   w1, w2: weights in `dtype` and `w_layout`;
  *   y, dx: fp32 T x d;  dw1, dw2: fp32, same shapes/layout as w1, w2.
