@@ -69,7 +69,13 @@ int main(void) {
 """
 
 
+def _gpu_visible():
+    import torch
+    return torch.cuda.device_count() > 0  # counts without initialising the runtime
+
+
 @pytest.mark.skipif(shutil.which("gcc") is None, reason="needs gcc")
+@pytest.mark.skipif(_gpu_visible(), reason="a host-only check: runs where no GPU is visible")
 def test_c_program_uses_the_abi(tmp_path):
     lib = os.path.join(LIB_DIR, "libtprank.so")
     if not os.path.exists(lib):
