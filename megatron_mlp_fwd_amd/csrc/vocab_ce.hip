@@ -313,7 +313,7 @@ __global__ __launch_bounds__(CP_NT) __attribute__((amdgpu_waves_per_eu(4, 4))) v
   // CE_STATS: per wave and shard, the maximum and the part A / part B sums
   // (each wave writes only its own row; the rows are combined in order).
   constexpr int TABW = CP_NW * CE_PMAX;
-  __shared__ float tab[STATS ? 3 * TABW : 1];
+  __shared__ float tab[STATS ? 4 * TABW : 1];
   __shared__ float red[CP_NW];
   __shared__ float red_a[CP_NW];
   __shared__ float red_b[CP_NW];
@@ -348,20 +348,23 @@ __global__ __launch_bounds__(CP_NT) __attribute__((amdgpu_waves_per_eu(4, 4))) v
   const bool tail = OPT && wid == 0 && lane < rem;
   if (tail) tail_sh[lane] = __uint_as_float((uint32_t)logits[row * V + 8 * nfull + lane] << 16);
   if constexpr (STATS)
-    for (int i = tid; i < 3 * TABW; i += CP_NT) tab[i] = i < TABW ? -INFINITY : 0.f;
+    for (int i = tid; i < 4 * TABW; i += CP_NT) tab[i] = i < 2 * TABW ? -INFINITY : 0.f;
 
   // CE_STATS: fold a group of 64 consecutive vectors [fv, fv + 64) (lane l
   // holds vector fv + l when `on`) into the per-shard tables.  Shards hold
   // vps >= 64 vectors, so at most two shards meet in a group.  A wave keeps
-  // one running value for its current shard cs and reduces it (DPP) into its
-  // table row when the shard changes; a group that straddles two shards is
-  // reduced once per shard.
+  // one running value for its current shard cs; within a pass it visits
+  // shards in increasing order, so each shard's value is complete when the
+  // wave moves past it and is reduced (DPP) and written into the wave's
+  // table row once per pass: a plain store, no read back.  A group that
+  // straddles two shards completes the first with the lanes before the
+  // boundary and starts the second with the rest.
   const int wid_u = __builtin_amdgcn_readfirstlane(wid);
   auto shard_flush = [&](auto max_, float r, int c, float* t) {
     constexpr bool MX = decltype(max_)::value;
     if (c < 0) return;
     const float w = MX ? wave_max(r) : wave_sum(r);
-    if (lane == 0) t[wid_u * CE_PMAX + c] = MX ? fmaxf(t[wid_u * CE_PMAX + c], w) : t[wid_u * CE_PMAX + c] + w;
+    if (lane == 0) t[wid_u * CE_PMAX + c] = w;
   };
   auto shard_acc = [&](auto max_, float x, bool on, int fv, float& run, int& cs, float* t) {
     constexpr bool MX = decltype(max_)::value;
@@ -369,32 +372,49 @@ __global__ __launch_bounds__(CP_NT) __attribute__((amdgpu_waves_per_eu(4, 4))) v
     const int lastv = fv + 63 < nvec - 1 ? fv + 63 : nvec - 1;
     const int sa = (int)__umulhi((uint32_t)fv, o.vps_magic), sb = (int)__umulhi((uint32_t)lastv, o.vps_magic);
     const float xv = on ? x : id;
-    if (sa == sb) {
-      if (sa != cs) {
-        shard_flush(max_, run, cs, t);
-        run = id;
-        cs = sa;
-      }
-      run = MX ? fmaxf(run, xv) : run + xv;
-    } else {
+    if (sa != cs) {  // the running shard is complete
       shard_flush(max_, run, cs, t);
       run = id;
-      cs = -1;
+      cs = sa;
+    }
+    if (sa == sb) {
+      run = MX ? fmaxf(run, xv) : run + xv;
+    } else {
       const bool in_b = fv + lane >= sb * o.vps;
-      shard_flush(max_, in_b ? id : xv, sa, t);
-      shard_flush(max_, in_b ? xv : id, sb, t);
+      const float xa = in_b ? id : xv;
+      run = MX ? fmaxf(run, xa) : run + xa;
+      shard_flush(max_, run, sa, t);
+      run = in_b ? xv : id;
+      cs = sb;
     }
   };
   using MaxOp = std::integral_constant<bool, true>;
   using SumOp = std::integral_constant<bool, false>;
-  float* const tabM = tab;
-  float* const tabA = tab + (STATS ? TABW : 0);
-  float* const tabB = tab + (STATS ? 2 * TABW : 0);
-  const int nli = (nlds + CP_NT - 1) / CP_NT;  // LDS-part groups per thread
+  float* const tabMA = tab;  // per wave and shard: maximum of part A, of part B, sums of part A, of part B
+  float* const tabMB = tab + (STATS ? TABW : 0);
+  float* const tabA = tab + (STATS ? 2 * TABW : 0);
+  float* const tabB = tab + (STATS ? 3 * TABW : 0);
+  // Which vectors each thread holds.  Plain and option instances: register
+  // slot s of thread tid holds vector s * CP_NT + tid (a workgroup's loads of
+  // one slot are one contiguous run), and the LDS part is walked the same way.
+  // CE_STATS: wave w holds the contiguous run [w RW, (w + 1) RW) of the
+  // register part (its slot s is vectors w RW + 64 s .. + 63) and walks the
+  // run [w RL, (w + 1) RL) of the LDS part, so a wave meets a shard boundary
+  // about once per pass instead of every few slots; each wave instruction
+  // still loads 64 consecutive vectors.
+  const int RW = STATS ? (nreg + 64 * CP_NW - 1) / (64 * CP_NW) * 64 : 0;
+  const int RL = STATS ? (nlds + 64 * CP_NW - 1) / (64 * CP_NW) * 64 : 0;
+  auto reg_vec = [&](int s, int t) { return STATS ? wid_u * RW + 64 * s + (t & 63) : s * CP_NT + t; };
+  auto reg_on = [&](int s, int t) { return (!STATS || 64 * s < RW) && reg_vec(s, t) < nreg; };
+  auto reg_fv = [&](int s) { return STATS ? wid_u * RW + 64 * s : s * CP_NT + 64 * wid_u; };
+  auto reg_grp = [&](int s) { return STATS ? 64 * s < RW && reg_fv(s) < nreg : reg_fv(s) < nvec; };
+  const int nli = STATS ? RL / 64 : (nlds + CP_NT - 1) / CP_NT;  // LDS-part groups per thread
+  auto lds_vec = [&](int i) { return STATS ? wid_u * RL + 64 * i + lane : i * CP_NT + tid; };
+  auto lds_fv = [&](int i) { return nreg + (STATS ? wid_u * RL + 64 * i : i * CP_NT + 64 * wid_u); };
 
   // Loads, in issue order: register slots [0, CP_RA), the LDS part, register
-  // slots [CP_RA, CP_RS).  Slot s of thread tid holds vector s * CP_NT + tid;
-  // lanes past the row end load zeros (out of range) and are skipped below.
+  // slots [CP_RA, CP_RS).  Lanes past the row end load zeros (out of range)
+  // and are skipped below.
   // Part A (the first slots, the LDS part and the tail) is reduced and
   // exponentiated against its own maximum m_A while part B still arrives;
   // part B then uses the row maximum m, and part A's values are scaled by
@@ -402,9 +422,9 @@ __global__ __launch_bounds__(CP_NT) __attribute__((amdgpu_waves_per_eu(4, 4))) v
   u32x4 v[CP_RS];
 #pragma unroll
   for (int s = 0; s < CP_RA; ++s) {
-    const int i = s * CP_NT + tid;
+    const int i = reg_vec(s, tid);
     v[s] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
-                                         rz, i < nreg ? (uint32_t)(16 * i) : CP_OOB, 0, 2));
+                                         rz, reg_on(s, tid) ? (uint32_t)(16 * i) : CP_OOB, 0, 2));
   }
   asm volatile("" ::: "memory");  // keep the issue order
   // LDS part: wave instruction j moves vectors nreg + 64 j .. + 63 (lanes past
@@ -415,9 +435,9 @@ __global__ __launch_bounds__(CP_NT) __attribute__((amdgpu_waves_per_eu(4, 4))) v
   asm volatile("" ::: "memory");
 #pragma unroll
   for (int s = CP_RA; s < CP_RS; ++s) {
-    const int i = s * CP_NT + tid;
+    const int i = reg_vec(s, tid);
     v[s] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
-                                         rz, i < nreg ? (uint32_t)(16 * i) : CP_OOB, 0, 2));
+                                         rz, reg_on(s, tid) ? (uint32_t)(16 * i) : CP_OOB, 0, 2));
   }
   // Only part B's loads may still be outstanding: this wave's DMA into LDS
   // and its part-A slots have landed.
@@ -431,19 +451,18 @@ __global__ __launch_bounds__(CP_NT) __attribute__((amdgpu_waves_per_eu(4, 4))) v
     int cs = -1;
 #pragma unroll
     for (int s = 0; s < CP_RA; ++s) {
-      const bool on = s * CP_NT + tid < nreg;
+      const bool on = reg_on(s, tid);
       const float x = on ? vec_max(v[s]) : -INFINITY;
       run = fmaxf(run, x);
-      const int fv = s * CP_NT + 64 * wid_u;
-      if (fv < nvec) shard_acc(MaxOp{}, x, on, fv, r, cs, tabM);
+      if (reg_grp(s)) shard_acc(MaxOp{}, x, on, reg_fv(s), r, cs, tabMA);
     }
     for (int i = 0; i < nli; ++i) {
-      const int j = i * CP_NT + tid, fv = nreg + i * CP_NT + 64 * wid_u;
+      const int j = lds_vec(i), fv = lds_fv(i);
       const float x = j < nlds ? vec_max(part[j]) : -INFINITY;
       run = fmaxf(run, x);
-      if (fv < nvec) shard_acc(MaxOp{}, x, j < nlds, fv, r, cs, tabM);
+      if (fv < nvec) shard_acc(MaxOp{}, x, j < nlds, fv, r, cs, tabMA);
     }
-    shard_flush(MaxOp{}, r, cs, tabM);
+    shard_flush(MaxOp{}, r, cs, tabMA);
   } else {
 #pragma unroll
     for (int s = 0; s < CP_RA; ++s)
@@ -491,21 +510,20 @@ __global__ __launch_bounds__(CP_NT) __attribute__((amdgpu_waves_per_eu(4, 4))) v
       int cs = -1;
 #pragma unroll
       for (int s = 0; s < CP_RA; ++s) {
-        const bool on = s * CP_NT + t2 < nreg;
+        const bool on = reg_on(s, t2);
         float vs = 0.f;
         if (on) expv(v[s], mAL, vs);
         sumA += vs;
-        const int fv = s * CP_NT + 64 * wid_u;
-        if (fv < nvec) shard_acc(SumOp{}, vs, on, fv, r, cs, tabA);
+        if (reg_grp(s)) shard_acc(SumOp{}, vs, on, reg_fv(s), r, cs, tabA);
         __builtin_amdgcn_sched_barrier(0);
       }
       for (int i = 0; i < nli; ++i) {
-        const int j = i * CP_NT + tid, fv = nreg + i * CP_NT + 64 * wid_u;
+        const int j = lds_vec(i), fv = lds_fv(i);
         float vs = 0.f;
         if (j < nlds) {
           u32x4 x = part[j];
           expv(x, mAL, vs);
-          part[j] = x;
+          part[j] = x;  // read in the gradient pass, after the next barriers
         }
         sumA += vs;
         if (fv < nvec) shard_acc(SumOp{}, vs, j < nlds, fv, r, cs, tabA);
@@ -532,13 +550,12 @@ __global__ __launch_bounds__(CP_NT) __attribute__((amdgpu_waves_per_eu(4, 4))) v
     int cs = -1;
 #pragma unroll
     for (int s = CP_RA; s < CP_RS; ++s) {
-      const bool on = s * CP_NT + t2 < nreg;
+      const bool on = reg_on(s, t2);
       const float x = on ? vec_max(v[s]) : -INFINITY;
       run = fmaxf(run, x);
-      const int fv = s * CP_NT + 64 * wid_u;
-      if (fv < nvec) shard_acc(MaxOp{}, x, on, fv, r, cs, tabM);
+      if (reg_grp(s)) shard_acc(MaxOp{}, x, on, reg_fv(s), r, cs, tabMB);
     }
-    shard_flush(MaxOp{}, r, cs, tabM);
+    shard_flush(MaxOp{}, r, cs, tabMB);
   } else {
 #pragma unroll
     for (int s = CP_RA; s < CP_RS; ++s)
@@ -560,12 +577,11 @@ __global__ __launch_bounds__(CP_NT) __attribute__((amdgpu_waves_per_eu(4, 4))) v
     int cs = -1;
 #pragma unroll
     for (int s = CP_RA; s < CP_RS; ++s) {
-      const bool on = s * CP_NT + t2 < nreg;
+      const bool on = reg_on(s, t2);
       float vs = 0.f;
       if (on) expv(v[s], mL, vs);
       sumB += vs;
-      const int fv = s * CP_NT + 64 * wid_u;
-      if (fv < nvec) shard_acc(SumOp{}, vs, on, fv, r, cs, tabB);
+      if (reg_grp(s)) shard_acc(SumOp{}, vs, on, reg_fv(s), r, cs, tabB);
       __builtin_amdgcn_sched_barrier(0);
     }
     shard_flush(SumOp{}, r, cs, tabB);
@@ -599,7 +615,7 @@ __global__ __launch_bounds__(CP_NT) __attribute__((amdgpu_waves_per_eu(4, 4))) v
     if (tid < o.P) {
       float mr = -INFINITY, sa = 0.f, sb = 0.f;
       for (int w = 0; w < CP_NW; ++w) {
-        mr = fmaxf(mr, tabM[w * CE_PMAX + tid]);
+        mr = fmaxf(mr, fmaxf(tabMA[w * CE_PMAX + tid], tabMB[w * CE_PMAX + tid]));
         sa += tabA[w * CE_PMAX + tid];
         sb += tabB[w * CE_PMAX + tid];
       }
@@ -632,8 +648,8 @@ __global__ __launch_bounds__(CP_NT) __attribute__((amdgpu_waves_per_eu(4, 4))) v
   bool owner = false;
 #pragma unroll
   for (int s = 0; s < CP_RS; ++s) {
-    const int i = s * CP_NT + t2;
-    if (i < nreg) {
+    const int i = reg_vec(s, t2);
+    if (reg_on(s, t2)) {
       owner |= i == vy;
       grad(v[s], i, s < CP_RA ? scaleA : scale);
     }
